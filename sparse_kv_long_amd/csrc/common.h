@@ -1,0 +1,84 @@
+// Device helpers shared by the gfx950 kernels: bf16 unpacking, the packed
+// bf16 dot product, wavefront reductions and the order-preserving float key.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace se {
+
+constexpr int kWave = 64;
+constexpr int kPage = 16;
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two bf16 in one dword: element 0 in the low half.
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// c + a.lo*b.lo + a.hi*b.hi with bf16 operands and fp32 accumulation
+// (v_dot2c_f32_bf16).  Products of two bf16 values are exact in fp32.
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
+
+__device__ __forceinline__ float dot8(const uint4& a, const uint4& b, float c) {
+  c = dot2(a.x, b.x, c);
+  c = dot2(a.y, b.y, c);
+  c = dot2(a.z, b.z, c);
+  c = dot2(a.w, b.w, c);
+  return c;
+}
+
+// DPP lane permutations inside a row of 16 lanes.
+//   0xB1: quad_perm [1,0,3,2] (lane ^ 1)     0x4E: quad_perm [2,3,0,1] (lane ^ 2)
+//   0x141: row_half_mirror (lane i <-> 7-i within 8)   0x140: row_mirror (i <-> 15-i)
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// All-reduce (sum) over aligned groups of N lanes, N in {1, 2, 4, 8, 16}.
+// Works for mirror pairings because every lane of a sub-group holds the same
+// value after the previous steps.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 2) v += dpp<0xB1>(v);
+  if constexpr (N >= 4) v += dpp<0x4E>(v);
+  if constexpr (N >= 8) v += dpp<0x141>(v);
+  if constexpr (N >= 16) v += dpp<0x140>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// 16-byte load with the non-temporal hint, for data read once per call.
+__device__ __forceinline__ uint4 ldnt16(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Order-preserving map of an fp32 to an unsigned key: a > b  <=>  key(a) > key(b)
+// for non-NaN values, with -0 taken as +0 so the two compare equal.
+__device__ __forceinline__ uint32_t float_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+}  // namespace se

@@ -1,0 +1,383 @@
+// Quest page summaries and page scoring for gfx950.
+//
+// Summaries (SparseEngine Fig. 3: the summaries Quest needs are attached to
+// each KV block; Table 8: 16-token pages): per physical page and KV head, the
+// channel-wise min and max of the keys of the page's valid tokens, stored as
+// bf16 [P, Hkv, 2, D] (row 0 min, row 1 max).
+//
+// Page score: each query head h bounds every logit of page p by
+//   U = s * sum_c max(q_c * min_c, q_c * max_c) = s * (q+ . max + q- . min)
+// with q+ = max(q, 0) and q- = min(q, 0) (exact: one term of each channel is
+// 0 * finite).  Both halves are bf16 dot products, so the score is 2D packed
+// v_dot2 operations per head.  The KV head's score is the max (or sum) of
+// its query heads' bounds.
+//
+// Work layout of the fast kernel: 8 lanes read one 2*D-element record with
+// 16-byte loads (a record of D = 128 is 512 B: lanes 0-7 read chunks 0-7,
+// then 8-15, ...), so one wave instruction covers 8 records; each lane owns
+// the same channel chunks of the min half and the max half, keeps q+ and q-
+// of those channels for all G heads in registers, and the 8 partial sums of
+// a record are combined with three DPP steps.
+#include "common.h"
+#include "se_internal.h"
+
+namespace se {
+
+// ---------------------------------------------------------------------------
+// K0: summaries of every valid page.  One thread per (page, head, 8 channels).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void summary_build_kernel(const uint16_t* __restrict__ k,
+                                                            const int32_t* __restrict__ page_table,
+                                                            const int32_t* __restrict__ seq_lens,
+                                                            uint16_t* __restrict__ summ, int B, int MP, int Hkv,
+                                                            int D, int64_t ps, int64_t hs, int64_t ts) {
+  const int cpr = D >> 3;
+  const int64_t col = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)B * MP * Hkv * cpr;
+  if (col >= total) return;
+  const int c8 = (int)(col % cpr);
+  int64_t r = col / cpr;
+  const int g = (int)(r % Hkv);
+  r /= Hkv;
+  const int lp = (int)(r % MP);
+  const int b = (int)(r / MP);
+  const int n = seq_lens[b];
+  if (lp * kPage >= n) return;
+  const int valid = min(kPage, n - lp * kPage);
+  const int64_t pid = page_table[(int64_t)b * MP + lp];
+  const uint16_t* src = k + pid * ps + (int64_t)g * hs + c8 * 8;
+  float mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mn[e] = __builtin_inff();
+    mx[e] = -__builtin_inff();
+  }
+  for (int t = 0; t < valid; ++t) {
+    const uint4 w = ld16(src + t * ts);
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mn[2 * e] = fminf(mn[2 * e], bf_lo(d[e]));
+      mx[2 * e] = fmaxf(mx[2 * e], bf_lo(d[e]));
+      mn[2 * e + 1] = fminf(mn[2 * e + 1], bf_hi(d[e]));
+      mx[2 * e + 1] = fmaxf(mx[2 * e + 1], bf_hi(d[e]));
+    }
+  }
+  uint32_t omn[4], omx[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    omn[e] = (__float_as_uint(mn[2 * e]) >> 16) | (__float_as_uint(mn[2 * e + 1]) & 0xffff0000u);
+    omx[e] = (__float_as_uint(mx[2 * e]) >> 16) | (__float_as_uint(mx[2 * e + 1]) & 0xffff0000u);
+  }
+  uint16_t* dst = summ + (pid * Hkv + g) * 2 * D + c8 * 8;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(omn[0], omn[1], omn[2], omn[3]);
+  *reinterpret_cast<uint4*>(dst + D) = make_uint4(omx[0], omx[1], omx[2], omx[3]);
+}
+
+hipError_t launch_build_summaries(const Layout& L, int B, int MP, const uint16_t* k, const int32_t* page_table,
+                                  const int32_t* seq_lens, uint16_t* summ, hipStream_t st) {
+  const int64_t total = (int64_t)B * MP * L.hkv * (L.dk / 8);
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(summary_build_kernel, dim3((unsigned)blocks), dim3(256), 0, st, k, page_table, seq_lens, summ,
+                     B, MP, L.hkv, L.dk, L.ps, L.hs, L.ts);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Shared pieces of the scoring kernels.
+// ---------------------------------------------------------------------------
+// Split a dword of two bf16 into its non-positive part (for the min row) and
+// its non-negative part (for the max row).
+__device__ __forceinline__ void split_sign(uint32_t w, uint32_t& neg, uint32_t& pos) {
+  const uint32_t s = w & 0x80008000u;
+  const uint32_t m = (s >> 15) * 0xffffu;  // 0xffff in each half whose sign is set
+  neg = w & m;
+  pos = w & ~m;
+}
+
+__device__ __forceinline__ uint4 split_neg(const uint4& w, uint4& pos) {
+  uint4 neg;
+  split_sign(w.x, neg.x, pos.x);
+  split_sign(w.y, neg.y, pos.y);
+  split_sign(w.z, neg.z, pos.z);
+  split_sign(w.w, neg.w, pos.w);
+  return neg;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// min/max over the valid keys of one page for 8 channels starting at `src`.
+__device__ __forceinline__ void minmax8(const uint16_t* src, int64_t ts, int valid, uint4& omn, uint4& omx) {
+  float mn[8], mx[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    mn[e] = __builtin_inff();
+    mx[e] = -__builtin_inff();
+  }
+  for (int t = 0; t < valid; ++t) {
+    const uint4 w = ld16(src + t * ts);
+    const uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      mn[2 * e] = fminf(mn[2 * e], bf_lo(d[e]));
+      mx[2 * e] = fmaxf(mx[2 * e], bf_lo(d[e]));
+      mn[2 * e + 1] = fminf(mn[2 * e + 1], bf_hi(d[e]));
+      mx[2 * e + 1] = fmaxf(mx[2 * e + 1], bf_hi(d[e]));
+    }
+  }
+  omn = make_uint4(pack_bf16(mn[0], mn[1]), pack_bf16(mn[2], mn[3]), pack_bf16(mn[4], mn[5]), pack_bf16(mn[6], mn[7]));
+  omx = make_uint4(pack_bf16(mx[0], mx[1]), pack_bf16(mx[2], mx[3]), pack_bf16(mx[4], mx[5]), pack_bf16(mx[6], mx[7]));
+}
+
+// ---------------------------------------------------------------------------
+// K1, register kernel: G * D <= 1024 (q+ and q- of the lane's channels of all
+// G heads stay in registers).  Grid (ceil(MP / (4*ppw)), Hkv, B), 4 waves per
+// block, each wave scores `ppw` consecutive pages of one (request, KV head).
+// With `refresh`, the wave holding the request's last page first rebuilds
+// that page's summary from its keys, stores it, and scores it from the
+// rebuilt values.
+// ---------------------------------------------------------------------------
+template <int G, int D, bool SUM>
+__global__ __launch_bounds__(256) void quest_score_reg_kernel(ScoreArgs a, int Hkv, int64_t ps, int64_t hs,
+                                                               int64_t ts, int ppw) {
+  constexpr int LPP = 8;
+  constexpr int NCH = D / 4;      // 16-byte chunks per record
+  constexpr int CPL = NCH / LPP;  // chunks per lane
+  constexpr int NCC = CPL / 2;    // channel chunks per lane
+  static_assert((D / 8) % LPP == 0, "channel chunks must split evenly over the 8 lanes of a record");
+
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 7, pg = lane >> 3;
+  const int n = a.seq_lens[b];
+  const int P = (n + kPage - 1) / kPage;
+  const bool dense = a.topk >= P;
+  const int start = (blockIdx.x * 4 + wave) * ppw;
+  int end = min(start + ppw, P);
+  if (start >= end) return;
+  const int plast = P - 1;
+  const bool do_refresh = a.refresh && plast >= start && plast < end;
+  if (dense && !do_refresh) return;
+  if (a.refresh) end = min(end, plast);
+
+  uint4 qn[G][NCC], qp[G][NCC];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + g * G + h) * D;
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) qn[h][cc] = split_neg(ld16(qrow + 8 * (j + LPP * cc)), qp[h][cc]);
+  }
+
+  const int64_t rec_stride = 2 * D;
+  const uint16_t* summ_g = a.summ + (int64_t)g * rec_stride;
+  float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
+  const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
+
+  auto page_score = [&](const uint4 (&d)[CPL]) -> float {
+    float acc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) acc[h] = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        acc[h] = dot8(qn[h][cc], d[cc], acc[h]);
+        acc[h] = dot8(qp[h][cc], d[NCC + cc], acc[h]);
+      }
+    }
+    float r = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float v = group_sum<LPP>(acc[h]);
+      r = (h == 0) ? v : (SUM ? r + v : fmaxf(r, v));
+    }
+    return r * a.scale;
+  };
+
+  if (!dense) {
+    constexpr int U = 2;
+    for (int p0 = start; p0 < end; p0 += 8 * U) {
+      int pid[U];
+      bool ok[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int p = p0 + 8 * u + pg;
+        ok[u] = p < end;
+        pid[u] = ok[u] ? ptrow[p] : 0;
+      }
+      uint4 d[U][CPL];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint16_t* rec = summ_g + (int64_t)pid[u] * Hkv * rec_stride + 8 * j;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) d[u][c] = ok[u] ? ld16(rec + 8 * LPP * c) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float sc = page_score(d[u]);
+        if (ok[u] && j == 0) srow[p0 + 8 * u + pg] = sc;
+      }
+    }
+  }
+
+  if (do_refresh) {
+    const int64_t pid = ptrow[plast];
+    const int valid = n - plast * kPage;
+    const uint16_t* kb = a.k + pid * ps + (int64_t)g * hs;
+    uint4 d[CPL];
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) minmax8(kb + 8 * (j + LPP * cc), ts, valid, d[cc], d[NCC + cc]);
+    uint16_t* rec = a.summ + (pid * Hkv + g) * rec_stride + 8 * j;
+    if (pg == 0) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) *reinterpret_cast<uint4*>(rec + 8 * LPP * c) = d[c];
+    }
+    const float sc = page_score(d);
+    if (!dense && lane == 0) srow[plast] = sc;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K1, generic kernel: any G <= 64 and D in {64, 128, 576}.  q+ and q- of all
+// heads live in LDS; each lane keeps its chunks of the record in registers
+// and loops over the heads.  Same grid and refresh rule as above.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void quest_score_lds_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs,
+                                                              int64_t ts, int ppw) {
+  constexpr int LPP = 8;
+  constexpr int NCH = D / 4;
+  constexpr int CPL = NCH / LPP;
+  constexpr int NCC = CPL / 2;
+  constexpr int DC = D / 8;  // channel chunks per head
+  static_assert(DC % LPP == 0, "channel chunks must split evenly over the 8 lanes of a record");
+  extern __shared__ uint4 qs[];  // [G][DC] q-  then [G][DC] q+
+
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j = lane & 7, pg = lane >> 3;
+  const int n = a.seq_lens[b];
+  const int P = (n + kPage - 1) / kPage;
+  const bool dense = a.topk >= P;
+  uint4* qneg = qs;
+  uint4* qpos = qs + G * DC;
+  for (int i = threadIdx.x; i < G * DC; i += blockDim.x) {
+    const int h = i / DC, c = i % DC;
+    uint4 pos;
+    qneg[i] = split_neg(ld16(a.q + ((int64_t)b * a.Hq + g * G + h) * D + 8 * c), pos);
+    qpos[i] = pos;
+  }
+  __syncthreads();
+
+  const int start = (blockIdx.x * 4 + wave) * ppw;
+  int end = min(start + ppw, P);
+  if (start >= end) return;
+  const int plast = P - 1;
+  const bool do_refresh = a.refresh && plast >= start && plast < end;
+  if (dense && !do_refresh) return;
+  if (a.refresh) end = min(end, plast);
+
+  const int64_t rec_stride = 2 * D;
+  const uint16_t* summ_g = a.summ + (int64_t)g * rec_stride;
+  float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
+  const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
+  const bool SUM = a.head_sum != 0;
+
+  auto page_score = [&](const uint4 (&d)[CPL]) -> float {
+    float r = 0.f;
+    for (int h = 0; h < G; ++h) {
+      float acc = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < NCC; ++cc) {
+        acc = dot8(qneg[h * DC + j + LPP * cc], d[cc], acc);
+        acc = dot8(qpos[h * DC + j + LPP * cc], d[NCC + cc], acc);
+      }
+      const float v = group_sum<LPP>(acc);
+      r = (h == 0) ? v : (SUM ? r + v : fmaxf(r, v));
+    }
+    return r * a.scale;
+  };
+
+  if (!dense) {
+    for (int p0 = start; p0 < end; p0 += 8) {
+      const int p = p0 + pg;
+      const bool ok = p < end;
+      const int64_t pid = ok ? ptrow[p] : 0;
+      uint4 d[CPL];
+      const uint16_t* rec = summ_g + pid * Hkv * rec_stride + 8 * j;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) d[c] = ok ? ld16(rec + 8 * LPP * c) : make_uint4(0, 0, 0, 0);
+      const float sc = page_score(d);
+      if (ok && j == 0) srow[p] = sc;
+    }
+  }
+
+  if (do_refresh) {
+    const int64_t pid = ptrow[plast];
+    const int valid = n - plast * kPage;
+    const uint16_t* kb = a.k + pid * ps + (int64_t)g * hs;
+    uint4 d[CPL];
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) minmax8(kb + 8 * (j + LPP * cc), ts, valid, d[cc], d[NCC + cc]);
+    uint16_t* rec = a.summ + (pid * Hkv + g) * rec_stride + 8 * j;
+    if (pg == 0) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) *reinterpret_cast<uint4*>(rec + 8 * LPP * c) = d[c];
+    }
+    const float sc = page_score(d);
+    if (!dense && lane == 0) srow[plast] = sc;
+  }
+}
+
+static int pick_ppw(int B, int Hkv, int MP) {
+  // about 2048 waves in flight (8 per CU); at least 32 pages per wave
+  const int64_t pages = (int64_t)B * Hkv * MP;
+  int64_t ppw = (pages + 2047) / 2048;
+  ppw = (ppw + 31) / 32 * 32;
+  if (ppw < 32) ppw = 32;
+  return (int)ppw;
+}
+
+template <int G, int D>
+static hipError_t launch_reg(const Layout& L, const ScoreArgs& a, hipStream_t st) {
+  const int ppw = pick_ppw(a.B, L.hkv, a.MP);
+  dim3 grid((a.MP + 4 * ppw - 1) / (4 * ppw), L.hkv, a.B);
+  if (a.head_sum)
+    hipLaunchKernelGGL((quest_score_reg_kernel<G, D, true>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, ppw);
+  else
+    hipLaunchKernelGGL((quest_score_reg_kernel<G, D, false>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, ppw);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_lds(const Layout& L, const ScoreArgs& a, int G, hipStream_t st) {
+  const int ppw = pick_ppw(a.B, L.hkv, a.MP);
+  dim3 grid((a.MP + 4 * ppw - 1) / (4 * ppw), L.hkv, a.B);
+  const size_t lds = (size_t)2 * G * (D / 8) * sizeof(uint4);
+  if (lds > 65536) {
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)quest_score_lds_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((quest_score_lds_kernel<D>), grid, dim3(256), lds, st, a, G, L.hkv, L.ps, L.hs, L.ts, ppw);
+  return hipGetLastError();
+}
+
+hipError_t launch_quest_scores(const Layout& L, const ScoreArgs& a, hipStream_t st) {
+  const int G = a.Hq / L.hkv;
+  if (a.B == 0 || a.MP == 0) return hipSuccess;
+#define SE_REG(GG, DD) \
+  if (G == GG && L.dk == DD) return launch_reg<GG, DD>(L, a, st);
+  SE_REG(1, 64) SE_REG(2, 64) SE_REG(4, 64) SE_REG(8, 64) SE_REG(16, 64)
+  SE_REG(1, 128) SE_REG(2, 128) SE_REG(4, 128) SE_REG(8, 128)
+#undef SE_REG
+  if (L.dk == 64) return launch_lds<64>(L, a, G, st);
+  if (L.dk == 128) return launch_lds<128>(L, a, G, st);
+  if (L.dk == 576) return launch_lds<576>(L, a, G, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace se

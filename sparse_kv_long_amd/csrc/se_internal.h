@@ -1,0 +1,79 @@
+// Internal launch interface between the C ABI (se_api.cpp) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace se {
+
+struct Layout {
+  int hkv, dk, dv, visk;
+  int64_t ps, hs, ts;  // page, head and token strides in elements
+};
+
+// ---- Quest -----------------------------------------------------------------
+hipError_t launch_build_summaries(const Layout& L, int B, int MP, const uint16_t* k, const int32_t* page_table,
+                                  const int32_t* seq_lens, uint16_t* summ, hipStream_t st);
+
+struct ScoreArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const int32_t* page_table;
+  uint16_t* summ;
+  const int32_t* seq_lens;
+  float* scores;
+  int B, Hq, MP, topk, refresh, head_sum;
+  float scale;
+};
+hipError_t launch_quest_scores(const Layout& L, const ScoreArgs& a, hipStream_t st);
+
+hipError_t launch_topk_pages(int B, int Hkv, int MP, int topk, const float* scores, const int32_t* seq_lens,
+                             int32_t* selected, hipStream_t st);
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* selected;  // nullptr = dense
+  float* out;
+  float* part_acc;  // [B, Hq, S, Dv]
+  float* part_ml;   // [B, Hq, S, 2]
+  int B, Hq, MP, topk, splits;
+  float scale;
+};
+int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, int requested);
+size_t decode_partials_bytes(const Layout& L, int B, int Hq, int splits);
+hipError_t launch_decode(const Layout& L, const DecodeArgs& a, hipStream_t st);
+
+// ---- SnapKV ----------------------------------------------------------------
+struct SnapArgs {
+  const uint16_t* q_win;  // [B, Hq, W, D]
+  const uint16_t* k;      // [B, Hkv, N, D]
+  const uint16_t* v;
+  const int32_t* lens;
+  int B, Hq, Hkv, D, N, W, pool, R, cap;
+  float scale;
+};
+struct SnapWork {
+  float* row_part;  // [B, Hkv, row_groups, nblk*waves, 128, 2] partial (max, sum)
+  float* row_c;     // [B, Hq, W]   log2-domain normaliser per window row
+  float* votes;     // [row_groups, B, Hkv, N]
+  float* pooled;    // [B, Hkv, N]
+};
+size_t snap_workspace_bytes(const SnapArgs& a);
+SnapWork snap_workspace_carve(const SnapArgs& a, void* ws);
+// skip_kept: requests whose prefix already fits the budget are not scored.
+hipError_t launch_snap_votes(const SnapArgs& a, const SnapWork& w, bool skip_kept, float* votes_out,
+                             hipStream_t st);
+hipError_t launch_maxpool(const SnapArgs& a, const float* votes, int row_groups, float* pooled,
+                          bool skip_kept, hipStream_t st);
+int snap_row_groups(const SnapArgs& a);
+hipError_t launch_snap_select(const SnapArgs& a, const float* pooled, int32_t* kept_idx, int32_t* kept_len,
+                              hipStream_t st);
+hipError_t launch_compact(const SnapArgs& a, const int32_t* kept_idx, const int32_t* kept_len, uint16_t* k_out,
+                          uint16_t* v_out, hipStream_t st);
+
+}  // namespace se

@@ -1,0 +1,375 @@
+// SnapKV eviction for gfx950: window scores, votes, max-pool and compaction.
+//
+// What is computed (SparseEngine Table 8: "32 scoring window; pooling kernel
+// 7"; Table 10: "probability-based prefill scores"; appendix Table 7: the
+// causal history [i] includes the current token; Table 15 note: physical
+// eviction releases KV storage).  For request b (prompt length n, L = n - W)
+// and KV head g, the G*W window rows (head hh, window index i, absolute
+// position L+i) have logits z_rj = s q_r . k_j over j <= L+i and are
+// normalised by a softmax over that history; the vote of prefix position
+// j < L is the sum of the rows' probabilities.
+//
+// The window x context logits are a dense contraction, so they run on the
+// matrix cores: v_mfma_f32_32x32x16_bf16 on 32 keys x 32 rows x 16 channels.
+// Two passes over the keys:
+//   pass 1 (rows x keys, keys as the MFMA M side): each lane holds one row and
+//          16 keys of a tile, so the running max and sum of 2^z per row are
+//          lane-local; partials per wave are merged by a small kernel into
+//          c_r = max_r + log2(sum_r), the row's log2 normaliser.
+//   pass 2 (rows as the M side): each lane holds one key and 16 rows, so the
+//          vote 2^(z - c_r) summed over rows is lane-local.  Only prefix keys
+//          j < L need votes and every window row sees all of them, so pass 2
+//          needs no causal mask.
+// One block handles a strided set of 32-key tiles of one (request, KV head,
+// row group of up to 128 rows), keeping the rows' q fragments in registers.
+#include "common.h"
+#include "se_internal.h"
+
+namespace se {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kRowsPerGroup = 128;
+constexpr int kSnapWaves = 4;
+
+__device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// Output element r (0..15) of a 32x32 MFMA tile held by lane `lane`: row
+// (M index) 8*(r/4) + 4*(lane/32) + r%4, column (N index) lane%32.
+__device__ __forceinline__ int mfma_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+struct SnapGeom {
+  int rows;   // G*W
+  int nrg;    // row groups of up to 128 rows
+  int nblk;   // blocks per (request, KV head, row group)
+  int slots;  // row-stat partials per (request, KV head, row group) = nblk * waves
+};
+
+static SnapGeom snap_geom(const SnapArgs& a) {
+  SnapGeom s;
+  s.rows = (a.Hq / a.Hkv) * a.W;
+  s.nrg = (s.rows + kRowsPerGroup - 1) / kRowsPerGroup;
+  const int units = a.B * a.Hkv * s.nrg;
+  int nblk = (512 + units - 1) / units;  // about 2048 waves in flight
+  const int tiles = (a.N + 31) / 32;
+  const int maxblk = (tiles + kSnapWaves - 1) / kSnapWaves;
+  if (nblk > maxblk) nblk = maxblk;
+  if (nblk < 1) nblk = 1;
+  s.nblk = nblk;
+  s.slots = nblk * kSnapWaves;
+  return s;
+}
+
+int snap_row_groups(const SnapArgs& a) { return snap_geom(a).nrg; }
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t snap_workspace_bytes(const SnapArgs& a) {
+  const SnapGeom s = snap_geom(a);
+  size_t bytes = 0;
+  bytes += align256((size_t)a.B * a.Hkv * s.nrg * s.slots * kRowsPerGroup * 2 * sizeof(float));
+  bytes += align256((size_t)a.B * a.Hq * a.W * sizeof(float));
+  bytes += align256((size_t)s.nrg * a.B * a.Hkv * a.N * sizeof(float));
+  bytes += align256((size_t)a.B * a.Hkv * a.N * sizeof(float));
+  return bytes;
+}
+
+SnapWork snap_workspace_carve(const SnapArgs& a, void* ws) {
+  const SnapGeom s = snap_geom(a);
+  char* p = static_cast<char*>(ws);
+  SnapWork w;
+  w.row_part = reinterpret_cast<float*>(p);
+  p += align256((size_t)a.B * a.Hkv * s.nrg * s.slots * kRowsPerGroup * 2 * sizeof(float));
+  w.row_c = reinterpret_cast<float*>(p);
+  p += align256((size_t)a.B * a.Hq * a.W * sizeof(float));
+  w.votes = reinterpret_cast<float*>(p);
+  p += align256((size_t)s.nrg * a.B * a.Hkv * a.N * sizeof(float));
+  w.pooled = reinterpret_cast<float*>(p);
+  return w;
+}
+
+// Load the q fragments of the block's row group: frag[rt][ks] holds, for
+// lane l, row rt*32 + l%32 and channels ks*16 + 8*(l/32) .. +7.
+template <int D, int NRT>
+__device__ __forceinline__ void load_q_frags(const SnapArgs& a, int b, int g, int rg, int rows, uint4 (&qf)[NRT][D / 16]) {
+  const int lane = threadIdx.x & 63;
+  const int G = a.Hq / a.Hkv;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int r = rg * kRowsPerGroup + rt * 32 + (lane & 31);
+    const bool ok = r < rows;
+    const int hh = ok ? r / a.W : 0, i = ok ? r % a.W : 0;
+    const uint16_t* qrow = a.q_win + (((int64_t)b * a.Hq + g * G + hh) * a.W + i) * D + 8 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[rt][ks] = ok ? ld16(qrow + 16 * ks) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// Key fragments of tile kt: lane l holds key kt*32 + l%32 (clamped to n-1)
+// and channels ks*16 + 8*(l/32) .. +7.
+template <int D>
+__device__ __forceinline__ void load_k_frags(const uint16_t* kbase, int kt, int n, uint4 (&kf)[D / 16]) {
+  const int lane = threadIdx.x & 63;
+  int key = kt * 32 + (lane & 31);
+  key = key < n ? key : n - 1;
+  const uint16_t* row = kbase + (int64_t)key * D + 8 * (lane >> 5);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) kf[ks] = ld16(row + 16 * ks);
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: partial row max / sum of 2^z (log2-domain logits).
+// Grid (nblk, Hkv * nrg, B), 4 waves.  Wave slot = blockIdx.x*4 + wave.
+// ---------------------------------------------------------------------------
+template <int D, int NRT>
+__global__ __launch_bounds__(256) void snap_rowstats_kernel(SnapArgs a, float* __restrict__ row_part, int nrg,
+                                                            int slots, int skip_kept, float scale2) {
+  const int b = blockIdx.z, g = blockIdx.y / nrg, rg = blockIdx.y % nrg;
+  const int n = a.lens[b];
+  const int L = n - a.W;
+  if (L <= 0 || (skip_kept && L <= a.R)) return;
+  const int G = a.Hq / a.Hkv;
+  const int rows = G * a.W;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = blockIdx.x * kSnapWaves + wave;
+
+  uint4 qf[NRT][D / 16];
+  load_q_frags<D, NRT>(a, b, g, rg, rows, qf);
+  // window position of this lane's row in each row tile (rows past G*W get
+  // L-1 so they see only the prefix; their statistics are never read)
+  int rpos[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int r = rg * kRowsPerGroup + rt * 32 + (lane & 31);
+    rpos[rt] = r < rows ? L + r % a.W : L - 1;
+  }
+  float m[NRT], l[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    m[rt] = -__builtin_inff();
+    l[rt] = 0.f;
+  }
+  const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + g) * a.N * D;
+  const int tiles = (n + 31) / 32;
+  for (int kt = slot; kt < tiles; kt += slots) {
+    uint4 kf[D / 16];
+    load_k_frags<D>(kbase, kt, n, kf);
+    const bool edge = kt * 32 + 31 >= L;  // tile reaches the window (or the end): mask per element
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      f32x16_t acc = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) acc = mfma32(kf[ks], qf[rt][ks], acc);
+      float z[16];
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        z[r] = acc[r] * scale2;
+        if (edge) {
+          const int key = kt * 32 + mfma_row(r, lane);
+          if (key > rpos[rt] || key >= n) z[r] = -__builtin_inff();
+        }
+        tmax = fmaxf(tmax, z[r]);
+      }
+      const float mn = fmaxf(m[rt], tmax);
+      if (mn != -__builtin_inff()) {
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(z[r] - mn);
+        l[rt] = l[rt] * __builtin_amdgcn_exp2f(m[rt] - mn) + s;
+        m[rt] = mn;
+      }
+    }
+  }
+  // combine the two lane halves (same rows, other 16 keys of each tile)
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const float mo = __shfl_xor(m[rt], 32), lo = __shfl_xor(l[rt], 32);
+    const float mn = fmaxf(m[rt], mo);
+    float ln = 0.f;
+    if (mn != -__builtin_inff())
+      ln = l[rt] * __builtin_amdgcn_exp2f(m[rt] - mn) + lo * __builtin_amdgcn_exp2f(mo - mn);
+    if (lane < 32) {
+      float* dst = row_part + (((((int64_t)b * a.Hkv + g) * nrg + rg) * slots + slot) * kRowsPerGroup + rt * 32 + lane) * 2;
+      dst[0] = mn;
+      dst[1] = ln;
+    }
+  }
+  // row tiles past NRT*32 inside the group do not exist; nothing else to write
+}
+
+// Merge the row-stat partials: c = max + log2(sum).  Grid (Hkv, B), 128 threads.
+__global__ __launch_bounds__(128) void snap_rowmerge_kernel(SnapArgs a, const float* __restrict__ row_part,
+                                                            float* __restrict__ row_c, int nrg, int slots, int skip_kept) {
+  const int b = blockIdx.y, g = blockIdx.x;
+  const int n = a.lens[b];
+  const int L = n - a.W;
+  if (L <= 0 || (skip_kept && L <= a.R)) return;
+  const int G = a.Hq / a.Hkv;
+  const int rows = G * a.W;
+  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
+    const int rg = r / kRowsPerGroup, rr = r % kRowsPerGroup;
+    const float* src = row_part + ((((int64_t)b * a.Hkv + g) * nrg + rg) * slots) * kRowsPerGroup * 2;
+    float M = -__builtin_inff();
+    for (int s = 0; s < slots; ++s) M = fmaxf(M, src[((int64_t)s * kRowsPerGroup + rr) * 2]);
+    float S = 0.f;
+    for (int s = 0; s < slots; ++s) {
+      const float ms = src[((int64_t)s * kRowsPerGroup + rr) * 2];
+      if (ms != -__builtin_inff()) S += src[((int64_t)s * kRowsPerGroup + rr) * 2 + 1] * __builtin_amdgcn_exp2f(ms - M);
+    }
+    const int hh = r / a.W, i = r % a.W;
+    row_c[((int64_t)b * a.Hq + g * G + hh) * a.W + i] = M + __builtin_amdgcn_logf(S);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: votes of prefix keys.  Grid (nblk, Hkv * nrg, B), 4 waves.
+// votes layout [nrg, B, Hkv, N].
+// ---------------------------------------------------------------------------
+template <int D, int NRT>
+__global__ __launch_bounds__(256) void snap_votes_kernel(SnapArgs a, const float* __restrict__ row_c,
+                                                         float* __restrict__ votes, int nrg, int slots, int skip_kept,
+                                                         float scale2) {
+  __shared__ float c_lds[kRowsPerGroup];
+  const int b = blockIdx.z, g = blockIdx.y / nrg, rg = blockIdx.y % nrg;
+  const int n = a.lens[b];
+  const int L = n - a.W;
+  if (L <= 0 || (skip_kept && L <= a.R)) return;
+  const int G = a.Hq / a.Hkv;
+  const int rows = G * a.W;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int slot = blockIdx.x * kSnapWaves + wave;
+  for (int r = threadIdx.x; r < kRowsPerGroup; r += blockDim.x) {
+    const int gr = rg * kRowsPerGroup + r;
+    // rows past G*W get +inf so their weight 2^(z - c) is 0
+    c_lds[r] = gr < rows ? row_c[((int64_t)b * a.Hq + g * G + gr / a.W) * a.W + gr % a.W] : __builtin_inff();
+  }
+  __syncthreads();
+
+  uint4 qf[NRT][D / 16];
+  load_q_frags<D, NRT>(a, b, g, rg, rows, qf);
+  const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + g) * a.N * D;
+  float* vrow = votes + (((int64_t)rg * a.B + b) * a.Hkv + g) * a.N;
+  const int tiles = (L + 31) / 32;
+  for (int kt = slot; kt < tiles; kt += slots) {
+    uint4 kf[D / 16];
+    load_k_frags<D>(kbase, kt, n, kf);
+    float vote = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      f32x16_t acc = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) acc = mfma32(qf[rt][ks], kf[ks], acc);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 c4 = *reinterpret_cast<const float4*>(&c_lds[rt * 32 + 8 * r4 + 4 * (lane >> 5)]);
+        vote += __builtin_amdgcn_exp2f(acc[4 * r4 + 0] * scale2 - c4.x);
+        vote += __builtin_amdgcn_exp2f(acc[4 * r4 + 1] * scale2 - c4.y);
+        vote += __builtin_amdgcn_exp2f(acc[4 * r4 + 2] * scale2 - c4.z);
+        vote += __builtin_amdgcn_exp2f(acc[4 * r4 + 3] * scale2 - c4.w);
+      }
+    }
+    vote += __shfl_xor(vote, 32);
+    const int key = kt * 32 + lane;
+    if (lane < 32 && key < L) vrow[key] = vote;
+  }
+}
+
+template <int D, int NRT>
+static hipError_t launch_votes_t(const SnapArgs& a, const SnapWork& w, const SnapGeom& s, int skip, float* votes,
+                                 hipStream_t st) {
+  const float scale2 = a.scale * kLog2e;
+  dim3 grid(s.nblk, a.Hkv * s.nrg, a.B);
+  hipLaunchKernelGGL((snap_rowstats_kernel<D, NRT>), grid, dim3(256), 0, st, a, w.row_part, s.nrg, s.slots, skip,
+                     scale2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(snap_rowmerge_kernel, dim3(a.Hkv, a.B), dim3(128), 0, st, a, w.row_part, w.row_c, s.nrg, s.slots,
+                     skip);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((snap_votes_kernel<D, NRT>), grid, dim3(256), 0, st, a, w.row_c, votes, s.nrg, s.slots, skip,
+                     scale2);
+  return hipGetLastError();
+}
+
+hipError_t launch_snap_votes(const SnapArgs& a, const SnapWork& w, bool skip_kept, float* votes_out,
+                             hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  const SnapGeom s = snap_geom(a);
+  const int nrt = (s.nrg > 1 ? kRowsPerGroup : s.rows + 31) / 32;  // row tiles per group
+  const int skip = skip_kept ? 1 : 0;
+#define SE_V(DD, RT) \
+  if (a.D == DD && nrt == RT) return launch_votes_t<DD, RT>(a, w, s, skip, votes_out, st);
+  SE_V(128, 1) SE_V(128, 2) SE_V(128, 3) SE_V(128, 4) SE_V(64, 1) SE_V(64, 2) SE_V(64, 3) SE_V(64, 4)
+#undef SE_V
+  return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Max-pool of the votes (summed over row groups).  One thread per position.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void maxpool_kernel(const float* __restrict__ votes, const int32_t* __restrict__ lens,
+                                                      float* __restrict__ pooled, int B, int Hkv, int N, int W,
+                                                      int R, int radius, int nrg, int skip_kept) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int L = lens[b] - W;
+  if (j >= L || (skip_kept && L <= R)) return;
+  const int lo = max(0, j - radius), hi = min(L - 1, j + radius);
+  float best = -__builtin_inff();
+  for (int t = lo; t <= hi; ++t) {
+    float s = 0.f;
+    for (int rg = 0; rg < nrg; ++rg) s += votes[(((int64_t)rg * B + b) * Hkv + g) * N + t];
+    best = fmaxf(best, s);
+  }
+  pooled[((int64_t)b * Hkv + g) * N + j] = best;
+}
+
+hipError_t launch_maxpool(const SnapArgs& a, const float* votes, int row_groups, float* pooled, bool skip_kept,
+                          hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  dim3 grid((a.N + 255) / 256, a.Hkv, a.B);
+  hipLaunchKernelGGL(maxpool_kernel, grid, dim3(256), 0, st, votes, a.lens, pooled, a.B, a.Hkv, a.N, a.W, a.R,
+                     a.pool / 2, row_groups, skip_kept ? 1 : 0);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Compaction: k_out[b][g][r] = k[b][g][kept[r]] for r < kept_len, same for v.
+// One thread per 16-byte chunk of a kept row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void compact_kernel(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                                      const int32_t* __restrict__ kept_idx,
+                                                      const int32_t* __restrict__ kept_len, uint16_t* __restrict__ k_out,
+                                                      uint16_t* __restrict__ v_out, int Hkv, int N, int D, int cap_idx,
+                                                      int cap_out) {
+  const int cpr = D / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int64_t bg = (int64_t)b * Hkv + g;
+  const int r = (int)(idx / cpr), c = (int)(idx % cpr);
+  if (r >= kept_len[bg]) return;
+  const int src = kept_idx[bg * cap_idx + r];
+  const int64_t so = (bg * N + src) * D + 8 * c;
+  const int64_t dofs = (bg * cap_out + r) * D + 8 * c;
+  *reinterpret_cast<uint4*>(k_out + dofs) = ld16(k + so);
+  *reinterpret_cast<uint4*>(v_out + dofs) = ld16(v + so);
+}
+
+hipError_t launch_compact(const SnapArgs& a, const int32_t* kept_idx, const int32_t* kept_len, uint16_t* k_out,
+                          uint16_t* v_out, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  const int cap_idx = a.R + a.W;
+  const int64_t chunks = (int64_t)cap_idx * (a.D / 8);
+  dim3 grid((unsigned)((chunks + 255) / 256), a.Hkv, a.B);
+  hipLaunchKernelGGL(compact_kernel, grid, dim3(256), 0, st, a.k, a.v, kept_idx, kept_len, k_out, v_out, a.Hkv, a.N,
+                     a.D, cap_idx, a.cap);
+  return hipGetLastError();
+}
+
+}  // namespace se

@@ -1,0 +1,216 @@
+// Top-k selection for gfx950: one 1024-thread block per (request, KV head).
+//
+// Selects the k largest of N fp32 scores, ties to the lower index, and writes
+// the chosen indices in ascending order.  Used for Quest's per-KV-head page
+// budget and for SnapKV's token budget (SparseEngine Table 8: Quest's
+// "selected" budgets over 16-token pages; SnapKV's selected tokens after the
+// 7-wide pooling).
+//
+// Method: scores map to order-preserving 32-bit keys held in registers (each
+// thread owns KPT consecutive indices).  Four 8-bit radix passes, each a
+// 256-bin LDS histogram of the keys that still match the chosen prefix, find
+// the exact k-th largest key T and how many keys equal to T must be taken.
+// Two block-wide exclusive scans then give every thread the number of
+// T-valued keys and of selected keys before it, so the selection (key > T,
+// or key == T among the first `need` such keys by index) is written in index
+// order without sorting.
+#include "common.h"
+#include "se_internal.h"
+
+namespace se {
+
+constexpr int kTopkThreads = 1024;
+
+struct TopkShared {
+  uint32_t hist[256];
+  int wave_tot[kTopkThreads / kWave];
+  int digit, above;
+};
+
+// Exclusive prefix sum over the block (1024 threads).
+__device__ __forceinline__ int block_exclusive_scan(int v, TopkShared& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sm.wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += sm.wave_tot[w];
+  __syncthreads();
+  return before + incl - v;
+}
+
+// Requires 0 < k < N <= KPT * 1024.  Writes k indices into out[0..k).
+template <int KPT>
+__device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t* __restrict__ out, TopkShared& sm) {
+  const int tid = threadIdx.x;
+  const int base = tid * KPT;
+  uint32_t key[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) key[i] = (base + i < N) ? float_key(row[base + i]) : 0u;
+
+  uint32_t prefix = 0, pmask = 0;
+  int rem = k;
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (tid < 256) sm.hist[tid] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KPT; ++i)
+      if (base + i < N && (key[i] & pmask) == prefix) atomicAdd(&sm.hist[(key[i] >> shift) & 255u], 1u);
+    __syncthreads();
+    if (tid < 64) {
+      const int c0 = sm.hist[4 * tid], c1 = sm.hist[4 * tid + 1], c2 = sm.hist[4 * tid + 2], c3 = sm.hist[4 * tid + 3];
+      const int local = c0 + c1 + c2 + c3;
+      int suf = local;  // count of bins >= 4*tid
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_down(suf, o);
+        if (tid + o < 64) suf += t;
+      }
+      const int above = suf - local;  // bins >= 4*tid + 4
+      const int s3 = above + c3, s2 = s3 + c2, s1 = s2 + c1, s0 = s1 + c0;
+      if (above < rem && s3 >= rem) {
+        sm.digit = 4 * tid + 3;
+        sm.above = above;
+      } else if (s3 < rem && s2 >= rem) {
+        sm.digit = 4 * tid + 2;
+        sm.above = s3;
+      } else if (s2 < rem && s1 >= rem) {
+        sm.digit = 4 * tid + 1;
+        sm.above = s2;
+      } else if (s1 < rem && s0 >= rem) {
+        sm.digit = 4 * tid;
+        sm.above = s1;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)sm.digit << shift;
+    pmask |= 255u << shift;
+    rem -= sm.above;
+  }
+  const uint32_t T = prefix;
+  const int need = rem;  // keys equal to T to take, lowest index first
+
+  int ceq = 0, cgt = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if (base + i < N) {
+      ceq += key[i] == T;
+      cgt += key[i] > T;
+    }
+  }
+  const int eq_before = block_exclusive_scan(ceq, sm);
+  const int take_eq = min(max(need - eq_before, 0), ceq);
+  int pos = block_exclusive_scan(cgt + take_eq, sm);
+  int eq_seen = eq_before;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    if (base + i < N) {
+      bool sel = key[i] > T;
+      if (key[i] == T) {
+        sel = eq_seen < need;
+        ++eq_seen;
+      }
+      if (sel) out[pos++] = base + i;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Quest: pages of (b, g).  P = ceil(seq_len/16); k' = min(topk, P); output
+// [B, Hkv, topk] ascending, padded with -1.
+// ---------------------------------------------------------------------------
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(const float* __restrict__ scores,
+                                                                  const int32_t* __restrict__ seq_lens,
+                                                                  int32_t* __restrict__ selected, int Hkv, int MP,
+                                                                  int topk) {
+  __shared__ TopkShared sm;
+  const int b = blockIdx.y, g = blockIdx.x;
+  const int n = seq_lens[b];
+  const int P = (n + kPage - 1) / kPage;
+  const int kk = min(topk, P);
+  int32_t* out = selected + ((int64_t)b * Hkv + g) * topk;
+  for (int i = kk + threadIdx.x; i < topk; i += blockDim.x) out[i] = -1;
+  if (kk == P) {
+    for (int i = threadIdx.x; i < P; i += blockDim.x) out[i] = i;
+    return;
+  }
+  block_topk<KPT>(scores + ((int64_t)b * Hkv + g) * MP, P, kk, out, sm);
+}
+
+static int pick_kpt(int n) {
+  int kpt = 1;
+  while (kpt * kTopkThreads < n) kpt <<= 1;
+  return kpt;
+}
+
+hipError_t launch_topk_pages(int B, int Hkv, int MP, int topk, const float* scores, const int32_t* seq_lens,
+                             int32_t* selected, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  dim3 grid(Hkv, B);
+  switch (pick_kpt(MP)) {
+#define SE_K(K)                                                                                                    \
+  case K:                                                                                                          \
+    hipLaunchKernelGGL(topk_pages_kernel<K>, grid, dim3(kTopkThreads), 0, st, scores, seq_lens, selected, Hkv, MP, \
+                       topk);                                                                                      \
+    break;
+    SE_K(1) SE_K(2) SE_K(4) SE_K(8) SE_K(16) SE_K(32) SE_K(64)
+#undef SE_K
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// SnapKV: prefix tokens of (b, g) by pooled vote.  L = n - W; if L <= R keep
+// 0..n-1; else keep top-R of pooled[0..L) then L..n-1.  Output kept_idx
+// [B, Hkv, R+W] ascending and -1 padded; kept_len [B, Hkv].
+// ---------------------------------------------------------------------------
+template <int KPT>
+__global__ __launch_bounds__(kTopkThreads) void snap_select_kernel(const float* __restrict__ pooled,
+                                                                   const int32_t* __restrict__ lens,
+                                                                   int32_t* __restrict__ kept_idx,
+                                                                   int32_t* __restrict__ kept_len, int Hkv, int N,
+                                                                   int W, int R) {
+  __shared__ TopkShared sm;
+  const int b = blockIdx.y, g = blockIdx.x;
+  const int n = lens[b];
+  const int L = n - W;
+  const int cap = R + W;
+  int32_t* out = kept_idx + ((int64_t)b * Hkv + g) * cap;
+  if (L <= R) {
+    for (int i = threadIdx.x; i < cap; i += blockDim.x) out[i] = i < n ? i : -1;
+    if (threadIdx.x == 0) kept_len[(int64_t)b * Hkv + g] = n;
+    return;
+  }
+  for (int i = threadIdx.x; i < W; i += blockDim.x) out[R + i] = L + i;
+  if (threadIdx.x == 0) kept_len[(int64_t)b * Hkv + g] = cap;
+  block_topk<KPT>(pooled + ((int64_t)b * Hkv + g) * N, L, R, out, sm);
+}
+
+hipError_t launch_snap_select(const SnapArgs& a, const float* pooled, int32_t* kept_idx, int32_t* kept_len,
+                              hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  dim3 grid(a.Hkv, a.B);
+  switch (pick_kpt(a.N - a.W)) {
+#define SE_K(K)                                                                                                   \
+  case K:                                                                                                         \
+    hipLaunchKernelGGL(snap_select_kernel<K>, grid, dim3(kTopkThreads), 0, st, pooled, a.lens, kept_idx, kept_len, \
+                       a.Hkv, a.N, a.W, a.R);                                                                     \
+    break;
+    SE_K(1) SE_K(2) SE_K(4) SE_K(8) SE_K(16) SE_K(32) SE_K(64)
+#undef SE_K
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace se

@@ -1,0 +1,150 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads on a machine without a GPU; these tests only exercise code
+paths that return before anything is enqueued: symbol exports, version and
+status strings, workspace-size queries and argument validation.
+"""
+import ctypes
+
+import pytest
+
+import sparse_kv_long_amd as se
+
+FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced on these paths
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return se.lib()
+
+
+def test_every_header_function_is_exported_and_wrapped(lib):
+    names = se.header_functions()
+    assert len(names) >= 14
+    for name in names:
+        assert hasattr(lib, name), name
+        assert callable(getattr(se, name)), name
+
+
+def test_version_and_status_strings(lib):
+    assert se.se_version() == 100
+    assert se.se_status_string(0) == "ok"
+    assert "invalid" in se.se_status_string(1)
+    assert "unsupported" in se.se_status_string(2)
+    assert "workspace" in se.se_status_string(3)
+    assert se.se_status_string(99) == "unknown status"
+
+
+def test_struct_sizes_match_header():
+    assert ctypes.sizeof(se.KvLayout) == 6 * 4 + 3 * 8
+    assert ctypes.sizeof(se.DecodeParams) == 8 * 4
+    assert ctypes.sizeof(se.SnapKVParams) == 10 * 4
+
+
+def rc_decode(layout, params, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, pt=FAKE, summ=FAKE, lens=FAKE, out=FAKE, sel=None, ws=FAKE, nbytes=1 << 40)
+    p.update(ptrs)
+    return se.lib().se_sparse_decode(ctypes.byref(layout), ctypes.byref(params), p["q"], p["k"], p["v"], p["pt"],
+                                     p["summ"], p["lens"], p["out"], p["sel"], p["ws"], p["nbytes"], None)
+
+
+def test_workspace_size_query():
+    L = se.paged_layout(4, 128, 128)
+    small = se.se_sparse_decode_workspace_size(L, se.decode_params(2, 32, 64, 8))
+    big = se.se_sparse_decode_workspace_size(L, se.decode_params(8, 32, 64, 8))
+    assert 0 < small < big
+    assert small % 256 == 0
+    sp = se.snapkv_params(2, 8, 2, 128, 1000, 32, 7, 64, 96)
+    assert se.se_snapkv_workspace_size(sp) > 2 * 2 * 1000 * 4
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda L, P: setattr(L, "page_size", 32), se.SE_EUNSUPPORTED),
+    (lambda L, P: setattr(L, "head_dim_qk", 96), se.SE_EUNSUPPORTED),
+    (lambda L, P: setattr(L, "head_dim_v", 64), se.SE_EUNSUPPORTED),
+    (lambda L, P: setattr(L, "v_is_k_prefix", 1), se.SE_EUNSUPPORTED),
+    (lambda L, P: setattr(L, "reserved", 1), se.SE_EINVAL),
+    (lambda L, P: setattr(L, "token_stride", 100), se.SE_EINVAL),
+    (lambda L, P: setattr(L, "token_stride", 64), se.SE_EINVAL),
+    (lambda L, P: setattr(L, "num_kv_heads", 0), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "num_q_heads", 30), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "num_q_heads", 12), se.SE_EUNSUPPORTED),
+    (lambda L, P: setattr(P, "topk", 0), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "batch", -1), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "max_pages_per_seq", 70000), se.SE_EUNSUPPORTED),
+    (lambda L, P: setattr(P, "sm_scale", -1.0), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "sm_scale", float("nan")), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "head_agg", 2), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "refresh_last_page", 3), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "num_splits", -2), se.SE_EINVAL),
+])
+def test_decode_argument_errors(mutate, code):
+    L = se.paged_layout(4, 128, 128)
+    P = se.decode_params(2, 32, 64, 8)
+    mutate(L, P)
+    assert rc_decode(L, P) == code
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "pt", "lens", "out", "summ"])
+def test_decode_null_pointers(which):
+    L = se.paged_layout(4, 128, 128)
+    P = se.decode_params(2, 32, 64, 8)
+    assert rc_decode(L, P, **{which: None}) == se.SE_EINVAL
+
+
+def test_decode_misaligned_and_workspace():
+    L = se.paged_layout(4, 128, 128)
+    P = se.decode_params(2, 32, 64, 8)
+    assert rc_decode(L, P, q=FAKE + 2) == se.SE_EINVAL
+    assert rc_decode(L, P, ws=None) == se.SE_EWORKSPACE
+    need = se.se_sparse_decode_workspace_size(L, P)
+    assert rc_decode(L, P, nbytes=need - 1) == se.SE_EWORKSPACE
+    assert rc_decode(L, P, ws=FAKE + 16) == se.SE_EWORKSPACE
+    # latent attention ignores v_pages; summaries may be NULL only when every request is dense
+    Lm = se.paged_layout(1, 576, 512, True)
+    Pm = se.decode_params(2, 32, 64, 64)
+    assert rc_decode(Lm, Pm, v=None, summ=None, nbytes=0) == se.SE_EWORKSPACE
+    Pm.refresh_last_page = 1
+    assert rc_decode(Lm, Pm, v=None, summ=None) == se.SE_EINVAL
+    # an empty batch is a no-op
+    P0 = se.decode_params(0, 32, 64, 8)
+    assert rc_decode(L, P0, q=None, ws=None) == se.SE_OK
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda p: setattr(p, "pool_kernel", 6), se.SE_EINVAL),
+    (lambda p: setattr(p, "pool_kernel", 0), se.SE_EINVAL),
+    (lambda p: setattr(p, "window", 0), se.SE_EINVAL),
+    (lambda p: setattr(p, "window", 65), se.SE_EUNSUPPORTED),
+    (lambda p: setattr(p, "budget", 0), se.SE_EINVAL),
+    (lambda p: setattr(p, "out_capacity", 95), se.SE_EINVAL),
+    (lambda p: setattr(p, "head_dim", 96), se.SE_EUNSUPPORTED),
+    (lambda p: setattr(p, "num_q_heads", 9), se.SE_EINVAL),
+    (lambda p: setattr(p, "num_q_heads", 2 * 33), se.SE_EUNSUPPORTED),
+    (lambda p: setattr(p, "max_prompt_len", 70000), se.SE_EUNSUPPORTED),
+])
+def test_snapkv_argument_errors(mutate, code):
+    p = se.snapkv_params(2, 8, 2, 128, 1000, 32, 7, 64, 96)
+    mutate(p)
+    rc = se.lib().se_snapkv_compact(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                    None)
+    assert rc == code
+
+
+def test_snapkv_pointer_and_workspace_errors():
+    p = se.snapkv_params(2, 8, 2, 128, 1000, 32, 7, 64, 96)
+    f = se.lib().se_snapkv_compact
+    assert f(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == se.SE_EINVAL
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == se.SE_EWORKSPACE
+    assert f(ctypes.byref(p), FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == se.SE_EINVAL
+    assert se.lib().se_maxpool1d(ctypes.byref(p), None, FAKE, FAKE, None) == se.SE_EINVAL
+    assert se.lib().se_snapkv_select(ctypes.byref(p), FAKE, None, FAKE, FAKE, None) == se.SE_EINVAL
+    assert se.lib().se_compact(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == se.SE_EINVAL
+
+
+def test_product_path_does_not_import_the_oracle():
+    import pathlib
+    pkg = pathlib.Path(se.__file__).parent
+    for f in list(pkg.glob("*.py")) + list(pkg.glob("csrc/*")):
+        text = f.read_text()
+        assert "oracle" not in text.replace("oracle-free", ""), f

@@ -1,0 +1,200 @@
+"""GPU parity of the Quest path (summaries, scores, top-k, decode) against the
+oracle, called through the C ABI, at sizes the oracle finishes in seconds.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_kv_long_amd as se
+from synth import QuestWorkload, TINY_QUEST, make_quest_inputs, bf16_bits
+from gpu_util import (DEV, announce, build_summaries, check_attention, check_selection, host_inputs, layout_for,
+                      params_for, run_sparse_decode, score_tolerance, sel_lists, to_np, workspace)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = {
+    "d64_g4": (QuestWorkload("t_d64_g4", 2, 8, 2, 64, 64, 700, 12, "heavy", seed=11), [700, 333]),
+    "d128_g8": (QuestWorkload("t_d128_g8", 3, 16, 2, 128, 128, 1500, 20, "zipf", seed=12), [1500, 1, 229]),
+    "d128_g4_outlier": (QuestWorkload("t_d128_g4", 2, 16, 4, 128, 128, 2048, 16, "outlier", seed=13), [2048, 1000]),
+    "d128_g1": (QuestWorkload("t_d128_g1", 2, 4, 4, 128, 128, 900, 10, "none", seed=14), [900, 17]),
+    "d128_g2": (QuestWorkload("t_d128_g2", 1, 8, 4, 128, 128, 640, 7, "none", seed=15), [640]),
+    "d128_g16": (QuestWorkload("t_d128_g16", 2, 32, 2, 128, 128, 800, 9, "none", seed=16), [800, 513]),
+    "d128_g32": (QuestWorkload("t_d128_g32", 1, 32, 1, 128, 128, 1200, 11, "none", seed=17), [1199]),
+    "d64_g16": (QuestWorkload("t_d64_g16", 1, 16, 1, 64, 64, 1000, 9, "none", seed=18), [1000]),
+    "mla": (QuestWorkload("t_mla", 2, 32, 1, 576, 512, 1000, 16, "none", v_is_k_prefix=True, seed=19), [1000, 455]),
+    "mla_g8": (QuestWorkload("t_mla_g8", 1, 8, 1, 576, 512, 600, 5, "none", v_is_k_prefix=True, seed=20), [600]),
+}
+
+
+def make(name, poison=True):
+    wl, lens = SMALL[name]
+    announce(f"quest case {name} seed {wl.seed} lens {lens}")
+    return wl, make_quest_inputs(wl, DEV, poison_tail=poison, seq_lens=lens, pool_extra=5)
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_summaries_exact(name):
+    wl, x = make(name)
+    summ = build_summaries(x, wl)
+    torch.cuda.synchronize()
+    h = host_inputs(x)
+    ref = oracle.quest_summaries(h["k"], h["pt"], h["lens"])
+    got = oracle.bf16_to_f64(bf16_bits(summ))
+    for b, n in enumerate(h["lens"]):
+        P = -(-int(n) // 16)
+        phys = h["pt"][b, :P]
+        np.testing.assert_array_equal(got[phys], ref[b, :P])
+        # bitwise as well (the data holds no zeros whose sign could differ)
+        ref_bits = (ref[b, :P].astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        assert (bf16_bits(summ)[phys] == ref_bits).all()
+
+
+@pytest.mark.parametrize("name", ["d64_g4", "d128_g8", "d128_g1", "d128_g16", "mla"])
+@pytest.mark.parametrize("head_agg", [0, 1])
+def test_scores_and_last_page_refresh(name, head_agg):
+    wl, x = make(name)
+    summ = build_summaries(x, wl)
+    h = host_inputs(x)
+    # corrupt every request's last-page summary; the refresh must rebuild it
+    for b, n in enumerate(h["lens"]):
+        P = -(-int(n) // 16)
+        summ[int(h["pt"][b, P - 1])] = 3.0
+    P = params_for(wl, refresh=1, head_agg=head_agg)
+    scores = torch.full((wl.batch, wl.num_kv_heads, wl.max_pages), float("nan"), device=DEV)
+    se.se_quest_scores(layout_for(wl), P, x["q"], x["k_pages"], x["page_table"], summ, x["seq_lens"], scores)
+    torch.cuda.synchronize()
+    ref_summ = oracle.quest_summaries(h["k"], h["pt"], h["lens"])
+    got_summ = oracle.bf16_to_f64(bf16_bits(summ))
+    A = oracle.quest_scores(h["q"], ref_summ, h["lens"], wl.group, wl.scale, mode="max" if head_agg == 0 else "sum")
+    qf = oracle.bf16_to_f64(h["q"])
+    S = to_np(scores)
+    for b, n in enumerate(h["lens"]):
+        Pb = -(-int(n) // 16)
+        np.testing.assert_array_equal(got_summ[h["pt"][b, :Pb]], ref_summ[b, :Pb])
+        for g in range(wl.num_kv_heads):
+            if wl.topk >= Pb:
+                assert np.isnan(S[b, g]).all(), "dense request must not be scored"
+                continue
+            tol = score_tolerance(qf[b, g * wl.group:(g + 1) * wl.group], ref_summ[b, :Pb, g, 0], ref_summ[b, :Pb, g, 1],
+                                  wl.scale)
+            if head_agg == 1:
+                tol = tol * wl.group
+            err = np.abs(S[b, g, :Pb] - A[b, g, :Pb])
+            assert (err <= tol).all(), f"b{b} g{g}: worst {np.max(err / tol):.3f} of tolerance"
+            assert np.isnan(S[b, g, Pb:]).all()
+
+
+@pytest.mark.parametrize("MP,topk", [(5, 2), (300, 17), (1024, 64), (3000, 256), (9000, 300), (20000, 2048),
+                                     (40000, 1000)])
+def test_topk_pages_exact(MP, topk):
+    announce(f"topk MP {MP} topk {topk}")
+    rng = np.random.default_rng(MP + topk)
+    B, Hkv = 3, 2
+    scores = rng.standard_normal((B, Hkv, MP)).astype(np.float32)
+    scores[0, 0] = rng.integers(0, 7, MP)  # heavy ties
+    scores[1, 1, ::3] = -0.0
+    scores[1, 1, 1::3] = 0.0
+    lens = np.array([MP * 16, MP * 16 - 5, max(1, MP * 8)], np.int32)
+    P = se.decode_params(B, Hkv, MP, topk)
+    sel = torch.full((B, Hkv, topk), 12345, dtype=torch.int32, device=DEV)
+    se.se_topk_pages(P, Hkv, torch.from_numpy(scores).to(DEV), torch.from_numpy(lens).to(DEV), sel)
+    torch.cuda.synchronize()
+    got = to_np(sel)
+    for b in range(B):
+        Pb = -(-int(lens[b]) // 16)
+        for g in range(Hkv):
+            want = oracle.unit_select(scores[b, g, :Pb].astype(np.float64), topk)
+            k = len(want)
+            assert (got[b, g, :k] == want).all(), f"b{b} g{g}"
+            assert (got[b, g, k:] == -1).all()
+
+
+def _decode_case(name, topk=None, splits=0):
+    wl, x = make(name)
+    summ = build_summaries(x, wl)
+    out, sel = run_sparse_decode(x, wl, summ, topk=topk, refresh=1, splits=splits)
+    h = host_inputs(x)
+    ref_summ = oracle.quest_summaries(h["k"], h["pt"], h["lens"])
+    A = oracle.quest_scores(h["q"], ref_summ, h["lens"], wl.group, wl.scale)
+    sel_np = to_np(sel)
+    k = wl.topk if topk is None else topk
+    for b, n in enumerate(h["lens"]):
+        Pb = -(-int(n) // 16)
+        for g in range(wl.num_kv_heads):
+            check_selection(sel_np[b, g], A[b, g, :Pb], k, f"{name} b{b} g{g}")
+    ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], sel_lists(sel_np, h["lens"]), wl.group,
+                                  wl.scale, wl.head_dim_v, wl.v_is_k_prefix)
+    return wl, x, out, sel, ref
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_sparse_decode_matches_oracle(name):
+    wl, x, out, sel, ref = _decode_case(name)
+    vmax = float(torch.nan_to_num(x["v_pages"] if x["v_pages"] is not None else x["k_pages"], 0.0).abs().max())
+    check_attention(to_np(out), ref, vmax, name)
+
+
+def test_tiny_quest_workload_full_size():
+    """The tiny 4K-token workload runs at its full size; heavy pages are kept."""
+    wl = TINY_QUEST
+    announce(f"tiny quest full size seed {wl.seed}")
+    x = make_quest_inputs(wl, DEV)
+    summ = build_summaries(x, wl)
+    out, sel = run_sparse_decode(x, wl, summ)
+    h = host_inputs(x)
+    ref_out, ref_sel, A = oracle.sparse_decode(h["q"], h["k"], h["v"], h["pt"], h["lens"], wl.topk, wl.group, wl.scale,
+                                               wl.head_dim_v)
+    sel_np = to_np(sel)
+    check_selection(sel_np[0, 0], A[0, 0], wl.topk, "tiny")
+    ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], sel_lists(sel_np, h["lens"]), wl.group,
+                                  wl.scale, wl.head_dim_v)
+    check_attention(to_np(out), ref, float(x["v_pages"].float().abs().max()), "tiny")
+
+
+@pytest.mark.parametrize("name", ["d64_g4", "d128_g8", "mla"])
+def test_dense_mode_equals_full_attention(name):
+    wl, x = make(name)
+    MP = wl.max_pages
+    out, sel = run_sparse_decode(x, wl, None, topk=MP, refresh=0)
+    h = host_inputs(x)
+    full = [[np.arange(-(-int(n) // 16)) for _ in range(wl.num_kv_heads)] for n in h["lens"]]
+    ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], full, wl.group, wl.scale, wl.head_dim_v,
+                                  wl.v_is_k_prefix)
+    sel_np = to_np(sel)
+    for b, n in enumerate(h["lens"]):
+        Pb = -(-int(n) // 16)
+        assert (sel_np[b, :, :Pb] == np.arange(Pb)).all() and (sel_np[b, :, Pb:] == -1).all()
+    check_attention(to_np(out), ref, 8.0, name)
+
+
+@pytest.mark.parametrize("name", ["d128_g8", "mla", "d64_g4"])
+def test_split_count_invariance_and_determinism(name):
+    wl, x = make(name)
+    summ = build_summaries(x, wl)
+    base = summ.clone()
+    outs = []
+    for splits in (1, 3, 0, 0):
+        summ.copy_(base)
+        o, s = run_sparse_decode(x, wl, summ, splits=splits)
+        outs.append((to_np(o), to_np(s)))
+    for o, s in outs[1:]:
+        assert (s == outs[0][1]).all()
+        np.testing.assert_allclose(o, outs[0][0], rtol=1e-5, atol=1e-6)
+    assert (outs[2][0] == outs[3][0]).all(), "repeated call not bitwise identical"
+
+
+def test_empty_and_single_token_requests():
+    wl = QuestWorkload("t_edge", 4, 8, 2, 128, 128, 64, 2, "none", seed=21)
+    announce("edge lengths [0, 1, 16, 17]")
+    x = make_quest_inputs(wl, DEV, poison_tail=True, seq_lens=[0, 1, 16, 17])
+    summ = build_summaries(x, wl)
+    out, sel = run_sparse_decode(x, wl, summ)
+    o = to_np(out)
+    assert (o[0] == 0).all()
+    h = host_inputs(x)
+    v0 = oracle.bf16_to_f64(h["v"][h["pt"][1, 0], :, 0, :])  # [Hkv, D]
+    np.testing.assert_allclose(o[1], np.repeat(v0, wl.group, axis=0), rtol=0, atol=1e-6)
+    ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], sel_lists(to_np(sel), h["lens"]),
+                                  wl.group, wl.scale, wl.head_dim_v)
+    check_attention(o, ref, 8.0, "edge")

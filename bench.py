@@ -8,9 +8,9 @@ last-page summary refresh, top-k per KV head, split-K attention over the kept
 pages and the split merge.
 
 Protocol: inputs are resident in HBM before timing; each timed step gets a
-fresh query and is preceded (outside its events) by a 1 GiB write that flushes
-the 256 MB Infinity Cache and the L2s; step time comes from HIP events on the
-launch stream.  Prints one JSON line.
+fresh query and is preceded (outside its events) by a 1 GiB read that evicts
+the 256 MB Infinity Cache and the L2s with clean lines; step time comes from
+HIP events on the launch stream.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -93,8 +93,12 @@ def main():
     gq = torch.Generator(device=dev)
     gq.manual_seed(wl.seed + 77)
     qs = torch.randn((nq, B, Hq, Dk), generator=gq, device=dev).to(torch.bfloat16)
-    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-    flush = None if args.no_flush else (lambda: flush_buf.fill_(1.0))
+    # cache flush: READ 1 GiB (4x the Infinity Cache) so the caches fill with
+    # clean lines; a write flush would leave dirty lines whose write-back
+    # then competes with the measured kernel
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    flush_sink = torch.empty((1,), dtype=torch.float32, device=dev)
+    flush = None if args.no_flush else (lambda: torch.sum(flush_buf, dim=(0,), keepdim=True, out=flush_sink))
     torch.cuda.synchronize()
 
     lens = x["seq_lens"].cpu().numpy().astype(np.int64)

@@ -51,6 +51,30 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// All-reduce over aligned groups of N lanes for any N in {1, 2, ..., 64}.
+template <int N>
+__device__ __forceinline__ float group_sum_any(float v) {
+  if constexpr (N <= 16) {
+    return group_sum<N>(v);
+  } else {
+    v = group_sum<16>(v);
+    v += __shfl_xor(v, 16);
+    if constexpr (N == 64) v += __shfl_xor(v, 32);
+    return v;
+  }
+}
+
+template <int N>
+__device__ __forceinline__ float group_max_any(float v) {
+  if constexpr (N >= 2) v = fmaxf(v, dpp<0xB1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp<0x4E>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp<0x141>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp<0x140>(v));
+  if constexpr (N >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  if constexpr (N >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -25,34 +25,42 @@ namespace se {
 
 template <int G, int DK, int DV>
 struct DecodeShape {
-  static constexpr int HW = G < (DK <= 128 ? 8 : 4) ? G : (DK <= 128 ? 8 : 4);  // heads per wave
-  static constexpr int NHG = G / HW;                                          // head groups
-  static constexpr int WPG = NHG >= 4 ? 1 : 4 / NHG;                          // waves per head group
-  static constexpr int NW = NHG * WPG;                                        // waves per block
-  static constexpr int LPT = DK <= 128 ? 4 : 8;                               // lanes per token, q.k
-  static constexpr int TPI = kWave / LPT;                                     // tokens per instruction
-  static constexpr int NCK = DK / LPT / 8;                                    // 16-byte chunks per lane
-  static constexpr int LPV = DV / 8;                                          // lanes per token, p.v
-  static constexpr int TPV = kWave / LPV;                                     // tokens per instruction
-  static constexpr int PPS = (DK <= 128 && G <= 16) ? 32 : 16;                // max pages per split
+  static constexpr int HWMAX = DK <= 128 ? 8 : 4;
+  static constexpr int HW = G < HWMAX ? G : HWMAX;           // heads per wave
+  static constexpr int NHG = G / HW;                          // head groups
+  static constexpr int WPG = NHG >= 4 ? 1 : 4 / NHG;          // waves per head group (they split the pages)
+  static constexpr int NW = NHG * WPG;                        // waves per block
+  static constexpr int LPT = DK <= 128 ? 4 : 8;               // lanes per token, q.k
+  static constexpr int TPI = kWave / LPT;                     // tokens per instruction, q.k
+  static constexpr int NTG = kPage / TPI;                     // token groups per page, q.k
+  static constexpr int NCK = DK / LPT / 8;                    // 16-byte chunks per lane, q.k
+  static constexpr int LPV = DV / 8;                          // lanes per token, p.v
+  static constexpr int TPV = kWave / LPV;                     // tokens per instruction, p.v
+  static constexpr int NTV = kPage / TPV;                     // token groups per page, p.v
+  static constexpr int PPS = (DK <= 128 && G <= 16) ? 32 : 16;  // max pages per split
+  static constexpr int PPW = (PPS + WPG - 1) / WPG;           // max pages per wave
+  static constexpr int LPH = kWave / HW;                      // lanes per head, softmax
+  static constexpr bool PREF_A = NTG * NCK * 4 <= 32;         // double-buffer K in registers
   static_assert(G % HW == 0, "group must split into whole head groups");
   static_assert(DK % (LPT * 8) == 0 && DV % 8 == 0 && LPV <= kWave, "unsupported head dims");
 };
 
+// Each wave runs q.k -> softmax -> p.v on its own pages with wave-private
+// LDS; the only block barriers are after the page-id staging and before the
+// final merge of the waves that share a head group.
 template <int G, int DK, int DV, bool VISK>
 __global__ __launch_bounds__((DecodeShape<G, DK, DV>::NW * 64)) void decode_kernel(DecodeArgs a, int Hkv, int64_t ps,
-                                                                                  int64_t hs, int64_t ts, int pps,
-                                                                                  float scale2) {
+                                                                                    int64_t hs, int64_t ts, int pps,
+                                                                                    float scale2) {
   using S = DecodeShape<G, DK, DV>;
-  constexpr int HW = S::HW, WPG = S::WPG, NW = S::NW, LPT = S::LPT, TPI = S::TPI, NCK = S::NCK;
-  constexpr int LPV = S::LPV, TPV = S::TPV, PPS = S::PPS;
-  constexpr int RED = WPG > 1 ? NW * HW * DV : 1;
+  constexpr int HW = S::HW, WPG = S::WPG, NW = S::NW, LPT = S::LPT, TPI = S::TPI, NTG = S::NTG, NCK = S::NCK;
+  constexpr int LPV = S::LPV, TPV = S::TPV, NTV = S::NTV, PPS = S::PPS, PPW = S::PPW, LPH = S::LPH;
 
-  __shared__ float s_lds[PPS * kPage * G];
-  __shared__ float red[RED];
+  __shared__ float s_lds[NW][PPW * kPage * HW];  // per wave: logits, then weights, token-major
+  __shared__ float comb[WPG > 1 ? NW * HW * DV : 1];
+  __shared__ float wml[NW][HW][2];
   __shared__ int64_t pid_lds[PPS];
   __shared__ int lp_lds[PPS];
-  __shared__ float ml_lds[G][2];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int n = a.seq_lens[b];
@@ -82,12 +90,14 @@ __global__ __launch_bounds__((DecodeShape<G, DK, DV>::NW * 64)) void decode_kern
   }
   __syncthreads();
 
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // wave index made scalar so that the page loops below branch on scalars
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int hg = w / WPG, pw = w % WPG;
   const int h0 = hg * HW;
-  const uint16_t* kg = a.k + (int64_t)g * hs;
+  const int npw = npg > pw ? (npg - pw + WPG - 1) / WPG : 0;  // pages of this wave: pw + WPG*ii
+  float* sw = s_lds[w];
 
-  // ---- phase A: logits ------------------------------------------------------
+  // ---- phase A: logits (log2 domain) -----------------------------------------
   {
     const int tok = lane / LPT, j = lane % LPT;
     uint4 qv[HW][NCK];
@@ -97,71 +107,105 @@ __global__ __launch_bounds__((DecodeShape<G, DK, DV>::NW * 64)) void decode_kern
 #pragma unroll
       for (int c = 0; c < NCK; ++c) qv[hh][c] = ld16(qrow + 8 * c * LPT);
     }
-    for (int i = pw; i < npg; i += WPG) {
-      const uint16_t* kb = kg + pid_lds[i] * ps + 8 * j;
-      const int pos0 = lp_lds[i] * kPage;
+    const uint16_t* kg = a.k + (int64_t)g * hs + 8 * j;
+    auto loadk = [&](int ii, uint4 (&kd)[NTG][NCK]) {
+      const uint16_t* kb = kg + pid_lds[pw + WPG * ii] * ps;
 #pragma unroll
-      for (int tg = 0; tg < kPage / TPI; ++tg) {
+      for (int tg = 0; tg < NTG; ++tg)
+#pragma unroll
+        for (int c = 0; c < NCK; ++c) kd[tg][c] = ldnt16(kb + (tg * TPI + tok) * ts + 8 * c * LPT);
+    };
+    auto scorek = [&](int ii, const uint4 (&kd)[NTG][NCK]) {
+      const int pos0 = lp_lds[pw + WPG * ii] * kPage;
+#pragma unroll
+      for (int tg = 0; tg < NTG; ++tg) {
         const int t = tg * TPI + tok;
-        uint4 kd[NCK];
-#pragma unroll
-        for (int c = 0; c < NCK; ++c) kd[c] = ld16(kb + t * ts + 8 * c * LPT);
         const bool valid = pos0 + t < n;
 #pragma unroll
         for (int hh = 0; hh < HW; ++hh) {
           float acc = 0.f;
 #pragma unroll
-          for (int c = 0; c < NCK; ++c) acc = dot8(qv[hh][c], kd[c], acc);
+          for (int c = 0; c < NCK; ++c) acc = dot8(qv[hh][c], kd[tg][c], acc);
           acc = group_sum<LPT>(acc) * scale2;
-          if (hh % LPT == j) s_lds[(i * kPage + t) * G + h0 + hh] = valid ? acc : -__builtin_inff();
+          if (hh % LPT == j) sw[(ii * kPage + t) * HW + hh] = valid ? acc : -__builtin_inff();
         }
+      }
+    };
+    if constexpr (S::PREF_A) {
+      // loads are unconditional (index clamped; a clamped load re-reads a
+      // cached page) so no branch sits between a prefetch and its use
+      uint4 kA[NTG][NCK], kB[NTG][NCK];
+      if (npw > 0) {
+        loadk(0, kA);
+        for (int ii = 0; ii < npw; ii += 2) {
+          loadk(min(ii + 1, npw - 1), kB);
+          __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+          scorek(ii, kA);
+          loadk(min(ii + 2, npw - 1), kA);
+          __builtin_amdgcn_sched_barrier(0);
+          if (ii + 1 < npw) scorek(ii + 1, kB);
+        }
+      }
+    } else {
+      for (int ii = 0; ii < npw; ++ii) {
+        uint4 kd[NTG][NCK];
+        loadk(ii, kd);
+        scorek(ii, kd);
       }
     }
   }
-  __syncthreads();
 
-  // ---- phase B: per-head max and exponentials ---------------------------------
-  const int T = npg * kPage;
-  for (int h = w; h < G; h += NW) {
+  // ---- value prefetch for the first page, then phase B -------------------------
+  const int vt = lane / LPV, vc = lane % LPV;
+  const uint16_t* vg = (VISK ? a.k : a.v) + (int64_t)g * hs + 8 * vc;
+  auto loadv = [&](int ii, uint4 (&vd)[NTV]) {
+    const uint16_t* vb = vg + pid_lds[pw + WPG * ii] * ps;
+#pragma unroll
+    for (int tg = 0; tg < NTV; ++tg) vd[tg] = ldnt16(vb + (tg * TPV + vt) * ts);
+  };
+  uint4 vA[NTV], vB[NTV];
+  if (npw > 0) loadv(0, vA);  // in flight during the softmax
+  __builtin_amdgcn_sched_barrier(0);
+
+  __builtin_amdgcn_wave_barrier();
+  {
+    const int T = npw * kPage;
+    const int hh = lane / LPH, r = lane % LPH;
     float m = -__builtin_inff();
-    for (int t = lane; t < T; t += kWave) m = fmaxf(m, s_lds[t * G + h]);
-    m = wave_max(m);
+    for (int t = r; t < T; t += LPH) m = fmaxf(m, sw[t * HW + hh]);
+    m = group_max_any<LPH>(m);
     float l = 0.f;
-    for (int t = lane; t < T; t += kWave) {
-      const float p = __builtin_amdgcn_exp2f(s_lds[t * G + h] - m);
-      s_lds[t * G + h] = p;
+    for (int t = r; t < T; t += LPH) {
+      const float p = __builtin_amdgcn_exp2f(sw[t * HW + hh] - m);
+      sw[t * HW + hh] = p;
       l += p;
     }
-    l = wave_sum(l);
-    if (lane == 0) {
-      ml_lds[h][0] = m;
-      ml_lds[h][1] = l;
+    l = group_sum_any<LPH>(l);
+    if (r == 0) {
+      wml[w][hh][0] = m;
+      wml[w][hh][1] = l;
     }
   }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
 
-  // ---- phase C: weighted values ----------------------------------------------
-  const int vt = lane / LPV, vc = lane % LPV;
+  // ---- phase C: weighted values -----------------------------------------------
   float acc[HW][8];
 #pragma unroll
   for (int hh = 0; hh < HW; ++hh)
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[hh][c] = 0.f;
-  const uint16_t* vg = (VISK ? a.k : a.v) + (int64_t)g * hs + 8 * vc;
-  for (int i = pw; i < npg; i += WPG) {
-    const uint16_t* vb = vg + pid_lds[i] * ps;
-    const int valid = min(kPage, n - lp_lds[i] * kPage);
+  auto accum = [&](int ii, const uint4 (&vd)[NTV]) {
+    const int valid = min(kPage, n - lp_lds[pw + WPG * ii] * kPage);
 #pragma unroll
-    for (int tg = 0; tg < kPage / TPV; ++tg) {
+    for (int tg = 0; tg < NTV; ++tg) {
       const int t = tg * TPV + vt;
-      const uint4 vd = ld16(vb + t * ts);
-      float vf[8] = {bf_lo(vd.x), bf_hi(vd.x), bf_lo(vd.y), bf_hi(vd.y),
-                     bf_lo(vd.z), bf_hi(vd.z), bf_lo(vd.w), bf_hi(vd.w)};
+      float vf[8] = {bf_lo(vd[tg].x), bf_hi(vd[tg].x), bf_lo(vd[tg].y), bf_hi(vd[tg].y),
+                     bf_lo(vd[tg].z), bf_hi(vd[tg].z), bf_lo(vd[tg].w), bf_hi(vd[tg].w)};
       if (valid < kPage && t >= valid) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) vf[c] = 0.f;  // slots past the sequence may hold anything
       }
-      const float* prow = s_lds + (i * kPage + t) * G + h0;
+      const float* prow = sw + (ii * kPage + t) * HW;
       float p[HW];
 #pragma unroll
       for (int hh = 0; hh < HW; ++hh) p[hh] = prow[hh];
@@ -170,6 +214,14 @@ __global__ __launch_bounds__((DecodeShape<G, DK, DV>::NW * 64)) void decode_kern
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[hh][c] = fmaf(p[hh], vf[c], acc[hh][c]);
     }
+  };
+  for (int ii = 0; ii < npw; ii += 2) {
+    loadv(min(ii + 1, npw - 1), vB);
+    __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+    accum(ii, vA);
+    loadv(min(ii + 2, npw - 1), vA);
+    __builtin_amdgcn_sched_barrier(0);
+    if (ii + 1 < npw) accum(ii + 1, vB);
   }
   // fold the TPV token groups of the wave
 #pragma unroll
@@ -189,26 +241,39 @@ __global__ __launch_bounds__((DecodeShape<G, DK, DV>::NW * 64)) void decode_kern
         *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[hh][4], acc[hh][5], acc[hh][6], acc[hh][7]);
       }
     }
+    if (lane < HW) {
+      a.part_ml[((head0 + h0 + lane) * nsplit + sbase) * 2] = wml[w][lane][0];
+      a.part_ml[((head0 + h0 + lane) * nsplit + sbase) * 2 + 1] = wml[w][lane][1];
+    }
   } else {
     if (vt == 0) {
 #pragma unroll
       for (int hh = 0; hh < HW; ++hh)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) red[((hg * WPG + pw) * HW + hh) * DV + 8 * vc + c] = acc[hh][c];
+        for (int c = 0; c < 8; ++c) comb[(w * HW + hh) * DV + 8 * vc + c] = acc[hh][c];
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < G * DV; idx += blockDim.x) {
-      const int h = idx / DV, c = idx % DV;
+    for (int idx = threadIdx.x; idx < G * (DV + 2); idx += blockDim.x) {
+      const int h = idx / (DV + 2), c = idx % (DV + 2);
       const int hgi = h / HW, hh = h % HW;
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int q = 0; q < WPG; ++q) M = fmaxf(M, wml[hgi * WPG + q][hh][0]);
       float s = 0.f;
 #pragma unroll
-      for (int q = 0; q < WPG; ++q) s += red[((hgi * WPG + q) * HW + hh) * DV + c];
-      a.part_acc[((head0 + h) * nsplit + sbase) * DV + c] = s;
+      for (int q = 0; q < WPG; ++q) {
+        const float mq = wml[hgi * WPG + q][hh][0];
+        const float f = mq == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mq - M);
+        const float v = c < DV ? comb[((hgi * WPG + q) * HW + hh) * DV + c] : wml[hgi * WPG + q][hh][1];
+        s += f * v;
+      }
+      if (c < DV)
+        a.part_acc[((head0 + h) * nsplit + sbase) * DV + c] = s;
+      else if (c == DV)
+        a.part_ml[((head0 + h) * nsplit + sbase) * 2] = M;
+      else
+        a.part_ml[((head0 + h) * nsplit + sbase) * 2 + 1] = s;
     }
-  }
-  for (int h = threadIdx.x; h < G; h += blockDim.x) {
-    a.part_ml[((head0 + h) * nsplit + sbase) * 2] = ml_lds[h][0];
-    a.part_ml[((head0 + h) * nsplit + sbase) * 2 + 1] = ml_lds[h][1];
   }
 }
 

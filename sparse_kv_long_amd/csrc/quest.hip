@@ -84,6 +84,8 @@ hipError_t launch_build_summaries(const Layout& L, int B, int MP, const uint16_t
   return hipGetLastError();
 }
 
+constexpr int kMaxPagesPerWave = 512;
+
 // ---------------------------------------------------------------------------
 // Shared pieces of the scoring kernels.
 // ---------------------------------------------------------------------------
@@ -147,18 +149,29 @@ __global__ __launch_bounds__(256) void quest_score_reg_kernel(ScoreArgs a, int H
   constexpr int NCH = D / 4;      // 16-byte chunks per record
   constexpr int CPL = NCH / LPP;  // chunks per lane
   constexpr int NCC = CPL / 2;    // channel chunks per lane
+  constexpr int U = 2;            // pages per lane group per stage (a stage is 8*U pages)
   static_assert((D / 8) % LPP == 0, "channel chunks must split evenly over the 8 lanes of a record");
+  __shared__ int32_t ids[4 * kMaxPagesPerWave];
 
   const int b = blockIdx.z, g = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int j = lane & 7, pg = lane >> 3;
   const int n = a.seq_lens[b];
   const int P = (n + kPage - 1) / kPage;
   const bool dense = a.topk >= P;
-  const int start = (blockIdx.x * 4 + wave) * ppw;
+  const int blk_start = blockIdx.x * 4 * ppw;
+  if (blk_start >= P) return;
+  const int blk_end = min(blk_start + 4 * ppw, P);
+  const int plast = P - 1;
+  const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
+  // stage the block's physical page ids in LDS (one coalesced pass)
+  if (!dense)
+    for (int i = threadIdx.x; i < blk_end - blk_start; i += blockDim.x) ids[i] = ptrow[blk_start + i];
+  __syncthreads();
+
+  const int start = blk_start + wave * ppw;
   int end = min(start + ppw, P);
   if (start >= end) return;
-  const int plast = P - 1;
   const bool do_refresh = a.refresh && plast >= start && plast < end;
   if (dense && !do_refresh) return;
   if (a.refresh) end = min(end, plast);
@@ -172,9 +185,9 @@ __global__ __launch_bounds__(256) void quest_score_reg_kernel(ScoreArgs a, int H
   }
 
   const int64_t rec_stride = 2 * D;
-  const uint16_t* summ_g = a.summ + (int64_t)g * rec_stride;
+  const uint16_t* summ_g = a.summ + (int64_t)g * rec_stride + 8 * j;
+  const int64_t pid_stride = (int64_t)Hkv * rec_stride;
   float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
-  const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
 
   auto page_score = [&](const uint4 (&d)[CPL]) -> float {
     float acc[G];
@@ -197,29 +210,38 @@ __global__ __launch_bounds__(256) void quest_score_reg_kernel(ScoreArgs a, int H
     return r * a.scale;
   };
 
-  if (!dense) {
-    constexpr int U = 2;
-    for (int p0 = start; p0 < end; p0 += 8 * U) {
-      int pid[U];
-      bool ok[U];
+  if (!dense && start < end) {
+    // Two register stages of 8*U pages: the next stage's loads are in flight
+    // while the current one is scored.  Loads are unconditional (page index
+    // clamped to the range; a clamped stage re-reads cached records) so that
+    // no branch sits between a load and its use; only the stores are masked.
+    const int nst = (end - start + 8 * U - 1) / (8 * U);
+    uint4 dA[U][CPL], dB[U][CPL];
+    auto load = [&](int st, uint4 (&d)[U][CPL]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int p = p0 + 8 * u + pg;
-        ok[u] = p < end;
-        pid[u] = ok[u] ? ptrow[p] : 0;
+        const int p = min(start + st * 8 * U + 8 * u + pg, end - 1);
+        const uint16_t* rec = summ_g + (int64_t)ids[p - blk_start] * pid_stride;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) d[u][c] = ldnt16(rec + 8 * LPP * c);
       }
-      uint4 d[U][CPL];
+    };
+    auto score = [&](int st, const uint4 (&d)[U][CPL]) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const uint16_t* rec = summ_g + (int64_t)pid[u] * Hkv * rec_stride + 8 * j;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) d[u][c] = ok[u] ? ld16(rec + 8 * LPP * c) : make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
+        const int p = start + st * 8 * U + 8 * u + pg;
         const float sc = page_score(d[u]);
-        if (ok[u] && j == 0) srow[p0 + 8 * u + pg] = sc;
+        if (p < end && j == 0) srow[p] = sc;
       }
+    };
+    load(0, dA);
+    for (int st = 0; st < nst; st += 2) {
+      load(min(st + 1, nst - 1), dB);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+      score(st, dA);
+      load(min(st + 2, nst - 1), dA);
+      __builtin_amdgcn_sched_barrier(0);
+      score(st + 1, dB);
     }
   }
 
@@ -333,11 +355,12 @@ __global__ __launch_bounds__(256) void quest_score_lds_kernel(ScoreArgs a, int G
 }
 
 static int pick_ppw(int B, int Hkv, int MP) {
-  // about 2048 waves in flight (8 per CU); at least 32 pages per wave
+  // about 2048 waves (8 per CU); between 32 and kMaxPagesPerWave pages each
   const int64_t pages = (int64_t)B * Hkv * MP;
   int64_t ppw = (pages + 2047) / 2048;
   ppw = (ppw + 31) / 32 * 32;
   if (ppw < 32) ppw = 32;
+  if (ppw > kMaxPagesPerWave) ppw = kMaxPagesPerWave;
   return (int)ppw;
 }
 

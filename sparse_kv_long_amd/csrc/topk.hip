@@ -7,9 +7,11 @@
 // 7-wide pooling).
 //
 // Method: scores map to order-preserving 32-bit keys held in registers (each
-// thread owns KPT consecutive indices).  Four 8-bit radix passes, each a
-// 256-bin LDS histogram of the keys that still match the chosen prefix, find
-// the exact k-th largest key T and how many keys equal to T must be taken.
+// thread owns KPT consecutive indices).  The bits common to every key are
+// found with a block-wide AND/OR; radix passes of up to 8 bits over the rest,
+// each a 256-bin LDS histogram of the keys that still match the chosen
+// prefix, find the exact k-th largest key T and how many keys equal to T must
+// be taken.
 // Two block-wide exclusive scans then give every thread the number of
 // T-valued keys and of selected keys before it, so the selection (key > T,
 // or key == T among the first `need` such keys by index) is written in index
@@ -24,6 +26,7 @@ constexpr int kTopkThreads = 1024;
 struct TopkShared {
   uint32_t hist[256];
   int wave_tot[kTopkThreads / kWave];
+  uint32_t wave_and[kTopkThreads / kWave], wave_or[kTopkThreads / kWave];
   int digit, above;
 };
 
@@ -44,24 +47,61 @@ __device__ __forceinline__ int block_exclusive_scan(int v, TopkShared& sm) {
   return before + incl - v;
 }
 
+// Block-wide AND and OR of a value.
+__device__ __forceinline__ void block_and_or(uint32_t& vand, uint32_t& vor, TopkShared& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    vand &= (uint32_t)__shfl_xor((int)vand, o);
+    vor |= (uint32_t)__shfl_xor((int)vor, o);
+  }
+  if (lane == 0) {
+    sm.wave_and[wave] = vand;
+    sm.wave_or[wave] = vor;
+  }
+  __syncthreads();
+  vand = 0xffffffffu;
+  vor = 0u;
+  for (int w = 0; w < kTopkThreads / kWave; ++w) {
+    vand &= sm.wave_and[w];
+    vor |= sm.wave_or[w];
+  }
+  __syncthreads();
+}
+
 // Requires 0 < k < N <= KPT * 1024.  Writes k indices into out[0..k).
 template <int KPT>
 __device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t* __restrict__ out, TopkShared& sm) {
   const int tid = threadIdx.x;
   const int base = tid * KPT;
   uint32_t key[KPT];
+  uint32_t kand = 0xffffffffu, kor = 0u;
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) key[i] = (base + i < N) ? float_key(row[base + i]) : 0u;
-
-  uint32_t prefix = 0, pmask = 0;
+  for (int i = 0; i < KPT; ++i) {
+    key[i] = (base + i < N) ? float_key(row[base + i]) : 0u;
+    if (base + i < N) {
+      kand &= key[i];
+      kor |= key[i];
+    }
+  }
+  // bits above the highest bit where the keys differ are common to all keys;
+  // the radix passes start below them (scores of one magnitude share their
+  // top byte, which would otherwise funnel every key into one bin)
+  block_and_or(kand, kor, sm);
+  const uint32_t diff = kand ^ kor;
+  uint32_t prefix = diff ? (kand & ~(0xffffffffu >> __builtin_clz(diff))) : kand;
+  uint32_t pmask = diff ? ~(0xffffffffu >> __builtin_clz(diff)) : 0xffffffffu;
   int rem = k;
+  int hi = diff ? 31 - __builtin_clz(diff) : -1;
 #pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  while (hi >= 0) {
+    const int lo = hi >= 7 ? hi - 7 : 0;
+    const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
     if (tid < 256) sm.hist[tid] = 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (base + i < N && (key[i] & pmask) == prefix) atomicAdd(&sm.hist[(key[i] >> shift) & 255u], 1u);
+      if (base + i < N && (key[i] & pmask) == prefix) atomicAdd(&sm.hist[(key[i] >> lo) & dmask], 1u);
     __syncthreads();
     if (tid < 64) {
       const int c0 = sm.hist[4 * tid], c1 = sm.hist[4 * tid + 1], c2 = sm.hist[4 * tid + 2], c3 = sm.hist[4 * tid + 3];
@@ -89,9 +129,10 @@ __device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t*
       }
     }
     __syncthreads();
-    prefix |= (uint32_t)sm.digit << shift;
-    pmask |= 255u << shift;
+    prefix |= (uint32_t)sm.digit << lo;
+    pmask |= dmask << lo;
     rem -= sm.above;
+    hi = lo - 1;
   }
   const uint32_t T = prefix;
   const int need = rem;  // keys equal to T to take, lowest index first

@@ -95,6 +95,8 @@ def test_topk_pages_exact(MP, topk):
     scores[0, 0] = rng.integers(0, 7, MP)  # heavy ties
     scores[1, 1, ::3] = -0.0
     scores[1, 1, 1::3] = 0.0
+    scores[2, 0] = 1.5  # every key equal
+    scores[2, 1] = np.float32(3.0) * (1 + (np.arange(MP) % 5 == 0))  # keys sharing their top bits
     lens = np.array([MP * 16, MP * 16 - 5, max(1, MP * 8)], np.int32)
     P = se.decode_params(B, Hkv, MP, topk)
     sel = torch.full((B, Hkv, topk), 12345, dtype=torch.int32, device=DEV)

@@ -18,6 +18,9 @@
 //            groups are then folded together with cross-lane shuffles.
 // The split writes (max, sum, unnormalised acc); the merge kernel combines the
 // splits of each head: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 #include "se_internal.h"
 
@@ -30,7 +33,7 @@ struct DecodeShape {
   static constexpr int NHG = G / HW;                          // head groups
   static constexpr int WPG = NHG >= 4 ? 1 : 4 / NHG;          // waves per head group (they split the pages)
   static constexpr int NW = NHG * WPG;                        // waves per block
-  static constexpr int LPT = DK <= 128 ? 4 : 8;               // lanes per token, q.k
+  static constexpr int LPT = 8;                               // lanes per token, q.k
   static constexpr int TPI = kWave / LPT;                     // tokens per instruction, q.k
   static constexpr int NTG = kPage / TPI;                     // token groups per page, q.k
   static constexpr int NCK = DK / LPT / 8;                    // 16-byte chunks per lane, q.k
@@ -49,7 +52,8 @@ struct DecodeShape {
 // LDS; the only block barriers are after the page-id staging and before the
 // final merge of the waves that share a head group.
 template <int G, int DK, int DV, bool VISK>
-__global__ __launch_bounds__((DecodeShape<G, DK, DV>::NW * 64)) void decode_kernel(DecodeArgs a, int Hkv, int64_t ps,
+__global__ __launch_bounds__((DecodeShape<G, DK, DV>::NW * 64))
+__attribute__((amdgpu_waves_per_eu(DK <= 128 ? 4 : 2))) void decode_kernel(DecodeArgs a, int Hkv, int64_t ps,
                                                                                     int64_t hs, int64_t ts, int pps,
                                                                                     float scale2) {
   using S = DecodeShape<G, DK, DV>;
@@ -277,6 +281,238 @@ __global__ __launch_bounds__((DecodeShape<G, DK, DV>::NW * 64)) void decode_kern
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core decode for Dk = Dv = 128 and G <= 16 (one 16-row head tile).
+//
+//   q.k   S[t][h] = sum_c K[t][c] q[h][c]: v_mfma_f32_16x16x32_bf16 with the
+//         page's 16 tokens as rows, 4 k-steps of 32 channels; lane l loads
+//         token l%16, channels 8*(l/16) + 32*ks (16 bytes).  Exact bf16
+//         products, fp32 accumulation.
+//   p.v   O[h][c] = sum_t P[h][t] V[t][c], one page (16 tokens) per
+//         v_mfma_f32_16x16x16_bf16 k-step: value rows are loaded whole
+//         (lane l: tokens 4e + l/16, channels 8*(l%16)..+7), so a lane owns 8
+//         channels of 4 tokens; N-tile nt takes channels {8n + nt}, which
+//         makes every B-fragment a 2 x v_perm_b32 repack of the lane's own
+//         registers.
+//         P enters as a hi + lo pair of bf16 (P = hi + lo to ~2^-16), so the
+//         weights keep near-fp32 precision at two MFMAs per tile.
+// Softmax, masking, the split partials and the merge are as in the VALU
+// kernel.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t dword(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+template <int G>
+struct MfmaDecodeShape {
+  static constexpr int PPS = G <= 8 ? 64 : 32;  // max pages per split
+};
+
+// One block of 4 waves per (split, KV head, request); wave w streams pages
+// w, w+4, ... of the split with an online softmax, keeping the K and V
+// loads of the next two pages in flight.  Lane l = 16*kq + col.
+//   q.k   A = K (lane: token col, channels 8kq + 32ks), B = q (head col);
+//         output lane (col, kq): tokens 4kq + i of the page, head col.
+//   p.v   A = P (lane: head col, tokens 4kq + e), B = V (lane: channels
+//         8col + nt, tokens 4kq + e) -- the weights stay in the lanes that
+//         computed them, and the value rows are loaded whole (16 lanes per
+//         256-byte row) and repacked in-lane with v_perm_b32.
+template <int G>
+__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts,
+                                                         int pps, float scale2) {
+  constexpr int D = 128, NW = 4, PPS = MfmaDecodeShape<G>::PPS;
+  static_assert(G <= 16, "one 16-row head tile");
+  __shared__ float comb[NW * G * D];
+  __shared__ float wml[NW][G][2];
+  __shared__ float alpha_lds[NW][16];
+  __shared__ int64_t pid_lds[PPS];
+  __shared__ int vld_lds[PPS];
+
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int n = a.seq_lens[b];
+  const int P = (n + kPage - 1) / kPage;
+  const int32_t* list = nullptr;
+  const int32_t* plist = nullptr;
+  int kk = P;
+  if (a.selected) {
+    kk = min(a.topk, P);
+    list = a.selected + ((int64_t)b * Hkv + g) * a.topk;
+    if (a.selected_phys) plist = a.selected_phys + ((int64_t)b * Hkv + g) * a.topk;
+  }
+  const int p_begin = split * pps;
+  const int npg = max(0, min(p_begin + pps, kk) - p_begin);
+  const int nsplit = gridDim.x;
+  const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
+  if (npg == 0) {
+    for (int h = threadIdx.x; h < G; h += blockDim.x) {
+      a.part_ml[((head0 + h) * nsplit + split) * 2] = -__builtin_inff();
+      a.part_ml[((head0 + h) * nsplit + split) * 2 + 1] = 0.f;
+    }
+    return;
+  }
+  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
+    const int lp = list ? list[p_begin + i] : p_begin + i;
+    pid_lds[i] = plist ? plist[p_begin + i] : a.page_table[(int64_t)b * a.MP + lp];
+    vld_lds[i] = min(kPage, n - lp * kPage);
+  }
+  __syncthreads();
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int npw = npg > w ? (npg - w + NW - 1) / NW : 0;  // pages of this wave: w + NW*ii
+  const uint16_t* kg = a.k + (int64_t)g * hs + col * ts + 8 * kq;
+  const uint16_t* vg = a.v + (int64_t)g * hs + 8 * col;
+
+  uint4 qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qf[ks] = col < G ? ld16(a.q + (head0 + col) * D + 8 * kq + 32 * ks) : make_uint4(0, 0, 0, 0);
+
+  struct PageRegs {
+    uint4 k[4], v[4];
+  };
+  auto load = [&](int ii, PageRegs& r) {
+    const int64_t off = pid_lds[w + NW * min(ii, npw - 1)] * ps;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) r.k[ks] = ldnt16(kg + off + 32 * ks);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r.v[e] = ldnt16(vg + off + (4 * kq + e) * ts);
+  };
+
+  float m_run = -__builtin_inff();  // running max of head col (log2 domain)
+  float l_run = 0.f;                // sum of 2^(z - m_run) over this lane's tokens
+  f32x4_t acc[8];                   // rows: heads 4kq + i; columns: channels 8col + nt
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto page = [&](int ii, PageRegs& r) {
+    const int valid = vld_lds[w + NW * ii];
+    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) s = mfma16(r.k[ks], qf[ks], s);
+    float z[4];
+    float pm = -__builtin_inff();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      z[i] = (col < G && 4 * kq + i < valid) ? s[i] * scale2 : -__builtin_inff();
+      pm = fmaxf(pm, z[i]);
+    }
+    pm = fmaxf(pm, __shfl_xor(pm, 16));
+    pm = fmaxf(pm, __shfl_xor(pm, 32));
+    const float m_new = fmaxf(m_run, pm);
+    const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
+    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    m_run = m_new;
+    // rescale the accumulators when some head's max moved (rows are heads 4kq + i)
+    if (__any(alpha != 1.f)) {
+      if (kq == 0) alpha_lds[w][col] = alpha;
+      __builtin_amdgcn_wave_barrier();
+      const float4 al = *reinterpret_cast<const float4*>(&alpha_lds[w][4 * kq]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        acc[nt][0] *= al.x;
+        acc[nt][1] *= al.y;
+        acc[nt][2] *= al.z;
+        acc[nt][3] *= al.w;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    // weights as hi + lo bf16 pairs, elements e = tokens 4kq + e
+    uint32_t hi[2], lo[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint32_t h0 = __float_as_uint(p[2 * d]) & 0xffff0000u, h1 = __float_as_uint(p[2 * d + 1]) & 0xffff0000u;
+      const uint32_t l0 = __float_as_uint(p[2 * d] - __uint_as_float(h0));
+      const uint32_t l1 = __float_as_uint(p[2 * d + 1] - __uint_as_float(h1));
+      hi[d] = (h0 >> 16) | h1;
+      lo[d] = (l0 >> 16) | (l1 & 0xffff0000u);
+    }
+    const bf16x4_t ph = __builtin_bit_cast(bf16x4_t, make_uint2(hi[0], hi[1]));
+    const bf16x4_t pl = __builtin_bit_cast(bf16x4_t, make_uint2(lo[0], lo[1]));
+    if (valid < kPage) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * kq + e >= valid) r.v[e] = make_uint4(0, 0, 0, 0);  // slots past the sequence may hold anything
+    }
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
+      const uint32_t f0 = __builtin_amdgcn_perm(dword(r.v[1], nt >> 1), dword(r.v[0], nt >> 1), sel);
+      const uint32_t f1 = __builtin_amdgcn_perm(dword(r.v[3], nt >> 1), dword(r.v[2], nt >> 1), sel);
+      const bf16x4_t vf = __builtin_bit_cast(bf16x4_t, make_uint2(f0, f1));
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vf, acc[nt], 0, 0, 0);
+      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vf, acc[nt], 0, 0, 0);
+    }
+  };
+
+  if (npw > 0) {
+    PageRegs r0, r1, r2;
+    load(0, r0);
+    load(1, r1);
+    for (int ii = 0; ii < npw; ii += 3) {
+      load(ii + 2, r2);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetches ahead of the compute
+      page(ii, r0);
+      load(ii + 3, r0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ii + 1 < npw) page(ii + 1, r1);
+      load(ii + 4, r1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ii + 2 < npw) page(ii + 2, r2);
+    }
+  }
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  // ---- merge the block's waves and write the split partial ------------------------
+  if (kq == 0 && col < G) {
+    wml[w][col][0] = m_run;
+    wml[w][col][1] = l_run;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * kq + i;
+    if (h < G) {
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) comb[(w * G + h) * D + 8 * col + nt] = acc[nt][i];
+    }
+  }
+  __syncthreads();
+  const int64_t sbase = (int64_t)split;
+  for (int idx = threadIdx.x; idx < G * (D + 2); idx += blockDim.x) {
+    const int h = idx / (D + 2), c = idx % (D + 2);
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int q = 0; q < NW; ++q) M = fmaxf(M, wml[q][h][0]);
+    float sacc = 0.f;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) {
+      const float mq = wml[q][h][0];
+      if (mq == -__builtin_inff()) continue;  // a wave without pages
+      const float v = c < D ? comb[(q * G + h) * D + c] : wml[q][h][1];
+      sacc += __builtin_amdgcn_exp2f(mq - M) * v;
+    }
+    if (c < D)
+      a.part_acc[((head0 + h) * nsplit + sbase) * D + c] = sacc;
+    else if (c == D)
+      a.part_ml[((head0 + h) * nsplit + sbase) * 2] = M;
+    else
+      a.part_ml[((head0 + h) * nsplit + sbase) * 2 + 1] = sacc;
+  }
+}
+
 // One block per (request, query head).
 __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part_acc,
                                                     const float* __restrict__ part_ml, float* __restrict__ out,
@@ -298,7 +534,16 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
   }
 }
 
-static int max_pps(const Layout& L, int G) { return (L.dk <= 128 && G <= 16) ? 32 : 16; }
+bool use_mfma_decode();
+
+static bool mfma_decode_shape(const Layout& L, int G) {
+  return L.dk == 128 && L.dv == 128 && !L.visk && G <= 16 && use_mfma_decode();
+}
+
+static int max_pps(const Layout& L, int G) {
+  if (mfma_decode_shape(L, G)) return G <= 8 ? 64 : 32;
+  return (L.dk <= 128 && G <= 16) ? 32 : 16;
+}
 
 int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, int requested) {
   // pages attended per (request, KV head) at most
@@ -307,7 +552,11 @@ int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, 
   const int units = B * L.hkv;
   const int mp = max_pps(L, Hq / L.hkv);
   const int smin = (kmax + mp - 1) / mp;
-  int s = requested > 0 ? requested : (1024 + units - 1) / units;
+  // about one full round of resident blocks (256 CUs x 2 blocks of the
+  // matrix-core kernel, x 4 of the VALU kernel): more splits only add per-block
+  // latency and merge traffic (measured), a partial second round idles the chip
+  const int target = mfma_decode_shape(L, Hq / L.hkv) ? 512 : 1024;
+  int s = requested > 0 ? requested : (target + units - 1) / units;
   if (s < smin) s = smin;
   if (s > kmax) s = kmax;
   const int pps = (kmax + s - 1) / s;
@@ -344,12 +593,43 @@ static hipError_t launch_d(const Layout& L, const DecodeArgs& a, int G, int pps,
   }
 }
 
+template <int G>
+static hipError_t launch_mfma_g(const Layout& L, const DecodeArgs& a, int pps, hipStream_t st) {
+  const float scale2 = a.scale * kLog2e;
+  dim3 grid(a.splits, L.hkv, a.B);
+  hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, pps, scale2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, st, a.part_acc, a.part_ml, a.out, a.splits, 128);
+  return hipGetLastError();
+}
+
+// Decode path: the matrix-core kernel for Dk = Dv = 128 and G <= 16 unless
+// SE_DECODE=valu; the VALU kernel for every other shape.
+bool use_mfma_decode() {
+  static const bool v = [] {
+    const char* e = getenv("SE_DECODE");
+    return !(e && strcmp(e, "valu") == 0);
+  }();
+  return v;
+}
+
 hipError_t launch_decode(const Layout& L, const DecodeArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int G = a.Hq / L.hkv;
   const int kmax = a.selected ? (a.topk < a.MP ? a.topk : a.MP) : a.MP;
   const int pps = (kmax + a.splits - 1) / a.splits;
   if (pps > max_pps(L, G)) return hipErrorInvalidValue;
+  if (mfma_decode_shape(L, G)) {
+    switch (G) {
+      case 1: return launch_mfma_g<1>(L, a, pps, st);
+      case 2: return launch_mfma_g<2>(L, a, pps, st);
+      case 4: return launch_mfma_g<4>(L, a, pps, st);
+      case 8: return launch_mfma_g<8>(L, a, pps, st);
+      case 16: return launch_mfma_g<16>(L, a, pps, st);
+      default: break;
+    }
+  }
   if (L.dk == 64 && L.dv == 64 && !L.visk) return launch_d<64, 64, false>(L, a, G, pps, st);
   if (L.dk == 128 && L.dv == 128 && !L.visk) return launch_d<128, 128, false>(L, a, G, pps, st);
   if (L.dk == 576 && L.dv == 512 && L.visk) return launch_d<576, 512, true>(L, a, G, pps, st);

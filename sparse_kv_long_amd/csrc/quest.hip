@@ -18,6 +18,9 @@
 // the same channel chunks of the min half and the max half, keeps q+ and q-
 // of those channels for all G heads in registers, and the 8 partial sums of
 // a record are combined with three DPP steps.
+#include <stdlib.h>
+#include <string.h>
+
 #include "common.h"
 #include "se_internal.h"
 
@@ -354,6 +357,223 @@ __global__ __launch_bounds__(256) void quest_score_lds_kernel(ScoreArgs a, int G
   }
 }
 
+// ---------------------------------------------------------------------------
+// K1, matrix-core kernel.  The page bound is a dense contraction,
+//   score[page][h] = sum_k rec[page][k] * qq[h][k],  k < 2D,
+// with rec = [min | max] (the stored summary record) and qq = [q- | q+], so
+// it runs on v_mfma_f32_16x16x32_bf16: 16 pages x 16 heads x 32 k per
+// instruction, fp32 accumulation of exact bf16 products.  Lane l supplies
+// page l%16 and k-chunk l/16 (+4 per k step) of the record, i.e. 16-byte
+// loads that form 64-byte contiguous runs; the output element i of lane l is
+// page 4*(l/16)+i, head l%16, so the KV-head max (or sum) is a 16-lane DPP
+// reduction.  qq fragments sit in registers (D <= 128) or in LDS (D = 576).
+// The wave that owns a request's last page rebuilds that page's summary from
+// its keys with all 64 lanes (each lane one 16-byte chunk: min or max of 8
+// channels over the valid tokens), stores it, and scores it from LDS.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                 0, 0, 0);
+}
+
+// qq fragment of head h for k-chunk ci (8 elements): q- of channels 8ci.. for
+// ci < D/8, q+ of channels 8(ci - D/8).. otherwise; zero for h >= G.
+__device__ __forceinline__ uint4 qq_chunk(const uint16_t* qrow_b, int h, int G, int D, int ci) {
+  if (h >= G) return make_uint4(0, 0, 0, 0);
+  const int dc = D / 8;
+  uint4 pos;
+  const uint4 neg = split_neg(ld16(qrow_b + (int64_t)h * D + 8 * (ci < dc ? ci : ci - dc)), pos);
+  return ci < dc ? neg : pos;
+}
+
+template <int D, int NT, bool BLDS, bool SUM>
+__global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs,
+                                                               int64_t ts, int ppw) {
+  constexpr int KS = 2 * D / 32;  // k steps per 16-page tile
+  constexpr int NCH = D / 4;      // 16-byte chunks per record
+  constexpr bool STAGE = D <= 128;  // records staged through LDS in the 8-lanes-per-record shape
+  extern __shared__ uint4 dyn_lds[];  // BLDS: qq fragments [NT][KS][64]
+  __shared__ int32_t ids[4 * kMaxPagesPerWave];
+  __shared__ uint4 refresh_rec[4][NCH];
+  __shared__ uint4 stage_lds[STAGE ? 4 * 16 * NCH : 1];
+
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int n = a.seq_lens[b];
+  const int P = (n + kPage - 1) / kPage;
+  const bool dense = a.topk >= P;
+  const int blk_start = blockIdx.x * 4 * ppw;
+  if (blk_start >= P) return;
+  const int blk_end = min(blk_start + 4 * ppw, P);
+  const int plast = P - 1;
+  const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
+  const uint16_t* qrow_b = a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
+  const int col = lane & 15, kq = lane >> 4;  // A: page slot / B: head; k-chunk quarter
+
+  if (!dense)
+    for (int i = threadIdx.x; i < blk_end - blk_start; i += blockDim.x) ids[i] = ptrow[blk_start + i];
+  if constexpr (BLDS) {
+    for (int i = threadIdx.x; i < NT * KS * 64; i += blockDim.x) {
+      const int l = i & 63, ks = (i >> 6) % KS, nt = (i >> 6) / KS;
+      dyn_lds[i] = qq_chunk(qrow_b, nt * 16 + (l & 15), G, D, (l >> 4) + 4 * ks);
+    }
+  }
+  __syncthreads();
+
+  const int start = blk_start + wave * ppw;
+  int end = min(start + ppw, P);
+  if (start >= end) return;
+  const bool do_refresh = a.refresh && plast >= start && plast < end;
+  if (dense && !do_refresh) return;
+  if (a.refresh) end = min(end, plast);
+
+  uint4 qb[BLDS ? 1 : NT][BLDS ? 1 : KS];
+  if constexpr (!BLDS) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qb[nt][ks] = qq_chunk(qrow_b, nt * 16 + col, G, D, kq + 4 * ks);
+  }
+  auto bfrag = [&](int nt, int ks) -> uint4 {
+    if constexpr (BLDS) return dyn_lds[(nt * KS + ks) * 64 + lane];
+    else return qb[nt][ks];
+  };
+
+  const uint16_t* summ_g0 = a.summ + (int64_t)g * 2 * D;
+  const uint16_t* summ_g = summ_g0 + 8 * kq;
+  const int64_t pid_stride = (int64_t)Hkv * 2 * D;
+  float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
+
+  // KV-head score of the 16 pages of a tile from the accumulators; lanes with
+  // col == 0 store pages base + 4*kq + i (if < lim)
+  auto finish = [&](const f32x4_t (&acc)[NT], int base, int lim) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bool real = nt * 16 + col < G;
+        const float x = real ? acc[nt][i] : (SUM ? 0.f : -__builtin_inff());
+        v = nt == 0 ? x : (SUM ? v + x : fmaxf(v, x));
+      }
+      v = SUM ? group_sum<16>(v) : group_max_any<16>(v);
+      const int p = base + 4 * kq + i;
+      if (col == 0 && p < lim) srow[p] = v * a.scale;
+    }
+  };
+
+  if (!dense && start < end) {
+    const int ntile = (end - start + 15) / 16;
+    if constexpr (STAGE) {
+      // Records are fetched 8 lanes per record (one full 128-byte line per
+      // lane group and instruction: lane l takes record l/8 of each half tile
+      // and chunks l%8 + 8c), written to this wave's LDS tile with chunk ci of
+      // page p stored at slot ci ^ p, and read back in the MFMA A layout, which
+      // the swizzle makes bank-conflict free.
+      constexpr int CPR = NCH / 8;  // chunks per lane per record
+      uint4* tile = stage_lds + wave * 16 * NCH;
+      const int r8 = lane >> 3, j8 = lane & 7;
+      uint4 dA[2][CPR], dB[2][CPR];
+      auto load = [&](int t, uint4 (&d)[2][CPR]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int p = min(start + 16 * t + 8 * u + r8, end - 1);
+          const uint16_t* rec = summ_g0 + (int64_t)ids[p - blk_start] * pid_stride + 8 * j8;
+#pragma unroll
+          for (int c = 0; c < CPR; ++c) d[u][c] = ldnt16(rec + 64 * c);
+        }
+      };
+      auto score = [&](int t, const uint4 (&d)[2][CPR]) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int pg = 8 * u + r8;
+#pragma unroll
+          for (int c = 0; c < CPR; ++c) tile[pg * NCH + ((j8 + 8 * c) ^ pg)] = d[u][c];
+        }
+        __builtin_amdgcn_wave_barrier();
+        f32x4_t acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 av = tile[col * NCH + ((kq + 4 * ks) ^ col)];
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(av, bfrag(nt, ks), acc[nt]);
+        }
+        __builtin_amdgcn_wave_barrier();
+        finish(acc, start + 16 * t, end);
+      };
+      load(0, dA);
+      for (int t = 0; t < ntile; t += 2) {
+        load(min(t + 1, ntile - 1), dB);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+        score(t, dA);
+        load(min(t + 2, ntile - 1), dA);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < ntile) score(t + 1, dB);
+      }
+    } else {
+      uint4 dA[KS], dB[KS];
+      auto load = [&](int t, uint4 (&d)[KS]) {
+        const int p = min(start + 16 * t + col, end - 1);
+        const uint16_t* rec = summ_g + (int64_t)ids[p - blk_start] * pid_stride;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) d[ks] = ldnt16(rec + 32 * ks);
+      };
+      auto score = [&](int t, const uint4 (&d)[KS]) {
+        f32x4_t acc[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) acc[nt] = mfma16(d[ks], bfrag(nt, ks), acc[nt]);
+        }
+        finish(acc, start + 16 * t, end);
+      };
+      load(0, dA);
+      for (int t = 0; t < ntile; t += 2) {
+        load(min(t + 1, ntile - 1), dB);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+        score(t, dA);
+        load(min(t + 2, ntile - 1), dA);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t + 1 < ntile) score(t + 1, dB);
+      }
+    }
+  }
+
+  if (do_refresh) {
+    const int64_t pid = ptrow[plast];
+    const int valid = n - plast * kPage;
+    const int dc = D / 8;
+    uint16_t* rec = a.summ + (pid * Hkv + g) * 2 * D;
+    for (int ci = lane; ci < NCH; ci += 64) {
+      uint4 mn, mx;
+      minmax8(a.k + pid * ps + (int64_t)g * hs + 8 * (ci < dc ? ci : ci - dc), ts, valid, mn, mx);
+      const uint4 v = ci < dc ? mn : mx;
+      *reinterpret_cast<uint4*>(rec + 8 * ci) = v;
+      refresh_rec[wave][ci] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (!dense) {
+      f32x4_t acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 d = col == 0 ? refresh_rec[wave][kq + 4 * ks] : make_uint4(0, 0, 0, 0);
+          acc[nt] = mfma16(d, bfrag(nt, ks), acc[nt]);
+        }
+      }
+      finish(acc, plast, plast + 1);  // page slot 0 of the tile is the last page
+    }
+  }
+}
+
 static int pick_ppw(int B, int Hkv, int MP) {
   // about 2048 waves (8 per CU); between 32 and kMaxPagesPerWave pages each
   const int64_t pages = (int64_t)B * Hkv * MP;
@@ -389,9 +609,47 @@ static hipError_t launch_lds(const Layout& L, const ScoreArgs& a, int G, hipStre
   return hipGetLastError();
 }
 
+template <int D, int NT, bool BLDS>
+static hipError_t launch_mfma(const Layout& L, const ScoreArgs& a, int G, hipStream_t st) {
+  const int ppw = pick_ppw(a.B, L.hkv, a.MP);
+  dim3 grid((a.MP + 4 * ppw - 1) / (4 * ppw), L.hkv, a.B);
+  const size_t lds = BLDS ? (size_t)NT * (2 * D / 32) * 64 * sizeof(uint4) : 0;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)quest_score_mfma_kernel<D, NT, BLDS, false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)quest_score_mfma_kernel<D, NT, BLDS, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (a.head_sum)
+    hipLaunchKernelGGL((quest_score_mfma_kernel<D, NT, BLDS, true>), grid, dim3(256), lds, st, a, G, L.hkv, L.ps, L.hs,
+                       L.ts, ppw);
+  else
+    hipLaunchKernelGGL((quest_score_mfma_kernel<D, NT, BLDS, false>), grid, dim3(256), lds, st, a, G, L.hkv, L.ps,
+                       L.hs, L.ts, ppw);
+  return hipGetLastError();
+}
+
+// Scoring path: the matrix-core kernel unless SE_QUEST_SCORE=valu selects
+// the VALU kernels (kept for comparison).
+static bool use_valu_scoring() {
+  static const bool v = [] {
+    const char* e = getenv("SE_QUEST_SCORE");
+    return e && strcmp(e, "valu") == 0;
+  }();
+  return v;
+}
+
 hipError_t launch_quest_scores(const Layout& L, const ScoreArgs& a, hipStream_t st) {
   const int G = a.Hq / L.hkv;
   if (a.B == 0 || a.MP == 0) return hipSuccess;
+  if (!use_valu_scoring()) {
+    if (L.dk == 64) return G <= 16 ? launch_mfma<64, 1, false>(L, a, G, st) : launch_mfma<64, 2, false>(L, a, G, st);
+    if (L.dk == 128) return G <= 16 ? launch_mfma<128, 1, false>(L, a, G, st) : launch_mfma<128, 2, false>(L, a, G, st);
+    if (L.dk == 576) return G <= 16 ? launch_mfma<576, 1, true>(L, a, G, st) : launch_mfma<576, 2, true>(L, a, G, st);
+    return hipErrorInvalidValue;
+  }
 #define SE_REG(GG, DD) \
   if (G == GG && L.dk == DD) return launch_reg<GG, DD>(L, a, st);
   SE_REG(1, 64) SE_REG(2, 64) SE_REG(4, 64) SE_REG(8, 64) SE_REG(16, 64)

@@ -64,7 +64,7 @@ float eff_scale(const se_kv_layout* L, const se_decode_params* p) {
 }
 
 struct DecodeWs {
-  size_t scores, sel, acc, ml, total;
+  size_t scores, sel, phys, acc, ml, total;
   int splits;
 };
 
@@ -77,7 +77,8 @@ DecodeWs decode_ws(const se_kv_layout* L, const se_decode_params* p, bool dense)
   const int smax = w.splits > s_other ? w.splits : s_other;
   w.scores = 0;
   w.sel = w.scores + align256((size_t)B * Hkv * MP * sizeof(float));
-  w.acc = w.sel + align256((size_t)B * Hkv * p->topk * sizeof(int32_t));
+  w.phys = w.sel + align256((size_t)B * Hkv * p->topk * sizeof(int32_t));
+  w.acc = w.phys + align256((size_t)B * Hkv * p->topk * sizeof(int32_t));
   w.ml = w.acc + align256((size_t)B * p->num_q_heads * smax * L->head_dim_v * sizeof(float));
   w.total = w.ml + align256((size_t)B * p->num_q_heads * smax * 2 * sizeof(float));
   return w;
@@ -190,6 +191,7 @@ int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params,
   char* ws = static_cast<char*>(workspace);
   float* scores = reinterpret_cast<float*>(ws + w.scores);
   int32_t* sel = selected ? selected : reinterpret_cast<int32_t*>(ws + w.sel);
+  int32_t* phys = reinterpret_cast<int32_t*>(ws + w.phys);
   const float scale = eff_scale(layout, params);
 
   if (need_scores) {
@@ -212,7 +214,7 @@ int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params,
   }
   if (!all_dense || selected) {
     rc = hip_status(se::launch_topk_pages(params->batch, L.hkv, params->max_pages_per_seq, params->topk, scores,
-                                          seq_lens, sel, st));
+                                          seq_lens, sel, page_table, all_dense ? nullptr : phys, st));
     if (rc) return rc;
   }
   se::DecodeArgs d;
@@ -222,6 +224,7 @@ int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params,
   d.page_table = page_table;
   d.seq_lens = seq_lens;
   d.selected = all_dense ? nullptr : sel;
+  d.selected_phys = all_dense ? nullptr : phys;
   d.out = out;
   d.part_acc = reinterpret_cast<float*>(ws + w.acc);
   d.part_ml = reinterpret_cast<float*>(ws + w.ml);
@@ -269,7 +272,7 @@ int se_topk_pages(const se_decode_params* params, int32_t num_kv_heads, const fl
   if (params->batch == 0) return SE_OK;
   if (!scores || !seq_lens || !selected) return SE_EINVAL;
   return hip_status(se::launch_topk_pages(params->batch, num_kv_heads, params->max_pages_per_seq, params->topk, scores,
-                                          seq_lens, selected, (hipStream_t)stream));
+                                          seq_lens, selected, nullptr, nullptr, (hipStream_t)stream));
 }
 
 int se_decode_selected(const se_kv_layout* layout, const se_decode_params* params, const void* q, const void* k_pages,
@@ -293,6 +296,7 @@ int se_decode_selected(const se_kv_layout* layout, const se_decode_params* param
   d.page_table = page_table;
   d.seq_lens = seq_lens;
   d.selected = selected;
+  d.selected_phys = nullptr;
   d.out = out;
   d.part_acc = reinterpret_cast<float*>(ws + w.acc);
   d.part_ml = reinterpret_cast<float*>(ws + w.ml);

@@ -28,8 +28,9 @@ struct ScoreArgs {
 };
 hipError_t launch_quest_scores(const Layout& L, const ScoreArgs& a, hipStream_t st);
 
+// phys (nullable): also write page_table[b][id] for every selected id
 hipError_t launch_topk_pages(int B, int Hkv, int MP, int topk, const float* scores, const int32_t* seq_lens,
-                             int32_t* selected, hipStream_t st);
+                             int32_t* selected, const int32_t* page_table, int32_t* phys, hipStream_t st);
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -37,7 +38,8 @@ struct DecodeArgs {
   const uint16_t* v;
   const int32_t* page_table;
   const int32_t* seq_lens;
-  const int32_t* selected;  // nullptr = dense
+  const int32_t* selected;       // nullptr = dense
+  const int32_t* selected_phys;  // physical ids of `selected`, or nullptr (looked up)
   float* out;
   float* part_acc;  // [B, Hq, S, Dv]
   float* part_ml;   // [B, Hq, S, 2]

@@ -69,9 +69,11 @@ __device__ __forceinline__ void block_and_or(uint32_t& vand, uint32_t& vor, Topk
   __syncthreads();
 }
 
-// Requires 0 < k < N <= KPT * 1024.  Writes k indices into out[0..k).
+// Requires 0 < k < N <= KPT * 1024.  Writes k indices into out[0..k) and,
+// when `translate` is given, translate[index] into out2[0..k).
 template <int KPT>
-__device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t* __restrict__ out, TopkShared& sm) {
+__device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t* __restrict__ out, TopkShared& sm,
+                           const int32_t* __restrict__ translate = nullptr, int32_t* __restrict__ out2 = nullptr) {
   const int tid = threadIdx.x;
   const int base = tid * KPT;
   uint32_t key[KPT];
@@ -157,7 +159,10 @@ __device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t*
         sel = eq_seen < need;
         ++eq_seen;
       }
-      if (sel) out[pos++] = base + i;
+      if (sel) {
+        if (out2) out2[pos] = translate[base + i];
+        out[pos++] = base + i;
+      }
     }
   }
 }
@@ -169,7 +174,9 @@ __device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t*
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(const float* __restrict__ scores,
                                                                   const int32_t* __restrict__ seq_lens,
-                                                                  int32_t* __restrict__ selected, int Hkv, int MP,
+                                                                  int32_t* __restrict__ selected,
+                                                                  const int32_t* __restrict__ page_table,
+                                                                  int32_t* __restrict__ phys, int Hkv, int MP,
                                                                   int topk) {
   __shared__ TopkShared sm;
   const int b = blockIdx.y, g = blockIdx.x;
@@ -177,12 +184,20 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(const float* _
   const int P = (n + kPage - 1) / kPage;
   const int kk = min(topk, P);
   int32_t* out = selected + ((int64_t)b * Hkv + g) * topk;
-  for (int i = kk + threadIdx.x; i < topk; i += blockDim.x) out[i] = -1;
+  int32_t* out2 = phys ? phys + ((int64_t)b * Hkv + g) * topk : nullptr;
+  const int32_t* ptrow = page_table ? page_table + (int64_t)b * MP : nullptr;
+  for (int i = kk + threadIdx.x; i < topk; i += blockDim.x) {
+    out[i] = -1;
+    if (out2) out2[i] = -1;
+  }
   if (kk == P) {
-    for (int i = threadIdx.x; i < P; i += blockDim.x) out[i] = i;
+    for (int i = threadIdx.x; i < P; i += blockDim.x) {
+      out[i] = i;
+      if (out2) out2[i] = ptrow[i];
+    }
     return;
   }
-  block_topk<KPT>(scores + ((int64_t)b * Hkv + g) * MP, P, kk, out, sm);
+  block_topk<KPT>(scores + ((int64_t)b * Hkv + g) * MP, P, kk, out, sm, ptrow, out2);
 }
 
 static int pick_kpt(int n) {
@@ -192,14 +207,14 @@ static int pick_kpt(int n) {
 }
 
 hipError_t launch_topk_pages(int B, int Hkv, int MP, int topk, const float* scores, const int32_t* seq_lens,
-                             int32_t* selected, hipStream_t st) {
+                             int32_t* selected, const int32_t* page_table, int32_t* phys, hipStream_t st) {
   if (B == 0) return hipSuccess;
   dim3 grid(Hkv, B);
   switch (pick_kpt(MP)) {
 #define SE_K(K)                                                                                                    \
   case K:                                                                                                          \
-    hipLaunchKernelGGL(topk_pages_kernel<K>, grid, dim3(kTopkThreads), 0, st, scores, seq_lens, selected, Hkv, MP, \
-                       topk);                                                                                      \
+    hipLaunchKernelGGL(topk_pages_kernel<K>, grid, dim3(kTopkThreads), 0, st, scores, seq_lens, selected,         \
+                       page_table, phys, Hkv, MP, topk);                                                           \
     break;
     SE_K(1) SE_K(2) SE_K(4) SE_K(8) SE_K(16) SE_K(32) SE_K(64)
 #undef SE_K

@@ -25,48 +25,70 @@ constexpr int kTopkThreads = 1024;
 
 struct TopkShared {
   uint32_t hist[256];
-  int wave_tot[kTopkThreads / kWave];
+  int wave_tot[2][kTopkThreads / kWave];
   uint32_t wave_and[kTopkThreads / kWave], wave_or[kTopkThreads / kWave];
-  int digit, above;
+  int digit, above, done;
 };
 
-// Exclusive prefix sum over the block (1024 threads).
-__device__ __forceinline__ int block_exclusive_scan(int v, TopkShared& sm) {
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
+}
+
+// Inclusive prefix sum over the wave with DPP: row_shr 1, 2, 4, 8 inside each
+// row of 16 lanes, then row_bcast 15 and 31 carry row totals forward.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += dpp_i<0x111>(x);
+  x += dpp_i<0x112>(x);
+  x += dpp_i<0x114>(x);
+  x += dpp_i<0x118>(x);
+  x += dpp_i<0x142, 0xa>(x);
+  x += dpp_i<0x143, 0xc>(x);
+  return x;
+}
+
+// Exclusive prefix sum over the block (1024 threads).  `buf` alternates
+// between calls so one barrier per call suffices.
+__device__ __forceinline__ int block_exclusive_scan(int v, TopkShared& sm, int buf) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  if (lane == 63) sm.wave_tot[wave] = incl;
+  const int incl = wave_incl_scan(v);
+  if (lane == 63) sm.wave_tot[buf][wave] = incl;
   __syncthreads();
   int before = 0;
-  for (int w = 0; w < wave; ++w) before += sm.wave_tot[w];
-  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kTopkThreads / kWave; ++w) before += w < wave ? sm.wave_tot[buf][w] : 0;
   return before + incl - v;
 }
 
-// Block-wide AND and OR of a value.
+// Block-wide AND and OR: DPP butterflies inside each row of 16 lanes, lane
+// reads across the four rows, then one pass over the per-wave results.
 __device__ __forceinline__ void block_and_or(uint32_t& vand, uint32_t& vor, TopkShared& sm) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    vand &= (uint32_t)__shfl_xor((int)vand, o);
-    vor |= (uint32_t)__shfl_xor((int)vor, o);
-  }
+  int a = (int)vand, o = (int)vor;
+  a &= dpp_i<0xB1>(a);
+  o |= dpp_i<0xB1>(o);
+  a &= dpp_i<0x4E>(a);
+  o |= dpp_i<0x4E>(o);
+  a &= dpp_i<0x141>(a);
+  o |= dpp_i<0x141>(o);
+  a &= dpp_i<0x140>(a);
+  o |= dpp_i<0x140>(o);
+  a = __builtin_amdgcn_readlane(a, 0) & __builtin_amdgcn_readlane(a, 16) & __builtin_amdgcn_readlane(a, 32) &
+      __builtin_amdgcn_readlane(a, 48);
+  o = __builtin_amdgcn_readlane(o, 0) | __builtin_amdgcn_readlane(o, 16) | __builtin_amdgcn_readlane(o, 32) |
+      __builtin_amdgcn_readlane(o, 48);
   if (lane == 0) {
-    sm.wave_and[wave] = vand;
-    sm.wave_or[wave] = vor;
+    sm.wave_and[wave] = (uint32_t)a;
+    sm.wave_or[wave] = (uint32_t)o;
   }
   __syncthreads();
   vand = 0xffffffffu;
   vor = 0u;
+#pragma unroll
   for (int w = 0; w < kTopkThreads / kWave; ++w) {
     vand &= sm.wave_and[w];
     vor |= sm.wave_or[w];
   }
-  __syncthreads();
 }
 
 // Requires 0 < k < N <= KPT * 1024.  Writes k indices into out[0..k) and,
@@ -77,15 +99,35 @@ __device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t*
   const int tid = threadIdx.x;
   const int base = tid * KPT;
   uint32_t key[KPT];
+  int32_t tr[KPT];
   uint32_t kand = 0xffffffffu, kor = 0u;
+  const bool full = base + KPT <= N;
+  if (KPT >= 4 && full && (((uintptr_t)row) & 15) == 0) {
+#pragma unroll
+    for (int i = 0; i < KPT; i += 4) {
+      const float4 f = *reinterpret_cast<const float4*>(row + base + i);
+      key[i] = float_key(f.x);
+      key[i + 1] = float_key(f.y);
+      key[i + 2] = float_key(f.z);
+      key[i + 3] = float_key(f.w);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) key[i] = (base + i < N) ? float_key(row[base + i]) : 0u;
+  }
+  // the translations are fetched with the keys, off the critical path
+  if (translate) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) tr[i] = (base + i < N) ? translate[base + i] : 0;
+  }
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    key[i] = (base + i < N) ? float_key(row[base + i]) : 0u;
     if (base + i < N) {
       kand &= key[i];
       kor |= key[i];
     }
   }
+  if (tid == 0) sm.done = 0;
   // bits above the highest bit where the keys differ are common to all keys;
   // the radix passes start below them (scores of one magnitude share their
   // top byte, which would otherwise funnel every key into one bin)
@@ -95,6 +137,9 @@ __device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t*
   uint32_t pmask = diff ? ~(0xffffffffu >> __builtin_clz(diff)) : 0xffffffffu;
   int rem = k;
   int hi = diff ? 31 - __builtin_clz(diff) : -1;
+  // Descend until the threshold bin is resolved: either every bit is fixed
+  // (ties broken by index below), or the bin holds exactly the `rem` keys
+  // still needed, in which case every key of the bin is taken.
 #pragma unroll 1
   while (hi >= 0) {
     const int lo = hi >= 7 ? hi - 7 : 0;
@@ -108,59 +153,62 @@ __device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t*
     if (tid < 64) {
       const int c0 = sm.hist[4 * tid], c1 = sm.hist[4 * tid + 1], c2 = sm.hist[4 * tid + 2], c3 = sm.hist[4 * tid + 3];
       const int local = c0 + c1 + c2 + c3;
-      int suf = local;  // count of bins >= 4*tid
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_down(suf, o);
-        if (tid + o < 64) suf += t;
-      }
-      const int above = suf - local;  // bins >= 4*tid + 4
+      const int incl = wave_incl_scan(local);
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      const int above = total - incl;  // bins >= 4*tid + 4
       const int s3 = above + c3, s2 = s3 + c2, s1 = s2 + c1, s0 = s1 + c0;
+      int d = -1, ab = 0, cnt = 0;
       if (above < rem && s3 >= rem) {
-        sm.digit = 4 * tid + 3;
-        sm.above = above;
+        d = 4 * tid + 3, ab = above, cnt = c3;
       } else if (s3 < rem && s2 >= rem) {
-        sm.digit = 4 * tid + 2;
-        sm.above = s3;
+        d = 4 * tid + 2, ab = s3, cnt = c2;
       } else if (s2 < rem && s1 >= rem) {
-        sm.digit = 4 * tid + 1;
-        sm.above = s2;
+        d = 4 * tid + 1, ab = s2, cnt = c1;
       } else if (s1 < rem && s0 >= rem) {
-        sm.digit = 4 * tid;
-        sm.above = s1;
+        d = 4 * tid, ab = s1, cnt = c0;
+      }
+      if (d >= 0) {
+        sm.digit = d;
+        sm.above = ab;
+        sm.done = (cnt == rem - ab) ? 1 : 0;
       }
     }
     __syncthreads();
     prefix |= (uint32_t)sm.digit << lo;
     pmask |= dmask << lo;
     rem -= sm.above;
+    if (sm.done) break;
     hi = lo - 1;
   }
-  const uint32_t T = prefix;
-  const int need = rem;  // keys equal to T to take, lowest index first
-
+  // selection: (key & pmask) > prefix, or == prefix among the first `rem` such
+  // keys by index (all of them when the descent stopped early)
+  const int need = rem;
+  const bool done = sm.done;
   int ceq = 0, cgt = 0;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     if (base + i < N) {
-      ceq += key[i] == T;
-      cgt += key[i] > T;
+      const uint32_t km = key[i] & pmask;
+      ceq += km == prefix;
+      cgt += km > prefix;
     }
   }
-  const int eq_before = block_exclusive_scan(ceq, sm);
-  const int take_eq = min(max(need - eq_before, 0), ceq);
-  int pos = block_exclusive_scan(cgt + take_eq, sm);
+  int eq_before = 0;
+  if (!done) eq_before = block_exclusive_scan(ceq, sm, 0);  // ties at full resolution only
+  const int take_eq = done ? ceq : min(max(need - eq_before, 0), ceq);
+  int pos = block_exclusive_scan(cgt + take_eq, sm, 1);
   int eq_seen = eq_before;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     if (base + i < N) {
-      bool sel = key[i] > T;
-      if (key[i] == T) {
+      const uint32_t km = key[i] & pmask;
+      bool sel = km > prefix;
+      if (km == prefix) {
         sel = eq_seen < need;
         ++eq_seen;
       }
       if (sel) {
-        if (out2) out2[pos] = translate[base + i];
+        if (out2) out2[pos] = tr[i];
         out[pos++] = base + i;
       }
     }

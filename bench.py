@@ -36,7 +36,10 @@ def parse():
     ap.add_argument("--workload", default="gqa32x4_d128_128k_b32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=6, help="(request, KV head) units the oracle times")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time the oracle baseline spends on sampled (request, KV head) units")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (HBM byte-counter calibration)")
     return ap.parse_args()
 
 
@@ -70,6 +73,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
 
     import sparse_kv_long_amd as se
     from synth import WORKLOADS, make_quest_inputs
@@ -200,52 +207,75 @@ def main():
     }
 
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, x, summ, qs[0], args.cpu_units)
+        result["cpu_baseline"] = cpu_baseline(wl, x, qs, args.cpu_seconds)
     print(json.dumps(result))
 
 
-def cpu_baseline(wl, x, summ, q, units):
+def copy_calibration(torch):
+    """A plain copy of 1 GiB (read 1 GiB, write 1 GiB), run three times: the
+    per-dispatch FETCH_SIZE / WRITE_SIZE it reports give the scale from those
+    counters to bytes."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
+
+
+def cpu_baseline(wl, x, qs, seconds):
     """Time the oracle's decode step (page bounds, KV-head scores, selection,
-    attention -- given the page summaries) on a few (request, KV head) units,
-    single-threaded, and scale to the whole step."""
+    attention -- given the page summaries, which the oracle builds beforehand,
+    untimed -- including the decoding of the bf16 inputs it reads) on (request, KV head) units in a seeded order,
+    single-threaded, until about `seconds` of CPU time are spent (passing on
+    to the next step's query once every unit of a step is done), and scale
+    to the whole step."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
     from synth import bf16_bits
 
-    G, D = wl.group, wl.head_dim_qk
-    rng = np.random.default_rng(0)
-    picks = [(int(b), int(g)) for b, g in zip(rng.integers(0, wl.batch, units), rng.integers(0, wl.num_kv_heads, units))]
+    G = wl.group
+    units = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    order = np.random.default_rng(0).permutation(len(units))
     pt = x["page_table"].cpu().numpy()
     lens = x["seq_lens"].cpu().numpy()
-    qh = bf16_bits(q)
     spent = 0.0
-    for b, g in picks:
+    done = 0
+    summaries = {}
+    while spent < seconds and done < len(units) * len(qs):
+        b, g = units[int(order[done % len(units)])]
+        qh = bf16_bits(qs[done // len(units)][b])
         n = int(lens[b])
         P = -(-n // 16)
         rows = torch_index(x["k_pages"], pt[b, :P], g)
         vrows = None if x["v_pages"] is None else torch_index(x["v_pages"], pt[b, :P], g)
-        sm = bf16_bits(summ[pt[b, :P].astype(np.int64), g])  # [P, 2, D]
-        mins, maxs = oracle.bf16_to_f64(sm[:, 0]), oracle.bf16_to_f64(sm[:, 1])
-        kp = oracle.bf16_to_f64(rows)
-        vp = kp[..., :wl.head_dim_v] if vrows is None else oracle.bf16_to_f64(vrows)
-        qf = oracle.bf16_to_f64(qh[b, g * G:(g + 1) * G])
+        if (b, g) not in summaries:  # prefill side (O1), untimed, by the oracle itself
+            summaries[(b, g)] = oracle.unit_summaries(oracle.gather_unit_pages(rows[:, None], np.arange(P), 0, n), n)
+        mins, maxs = summaries[(b, g)]
         with threadpool_limits(1):
             t0 = time.perf_counter()
+            qf = oracle.bf16_to_f64(qh[g * G:(g + 1) * G])
             U = oracle.unit_page_bounds(qf, mins, maxs, wl.scale)
             A = oracle.unit_kv_head_score(U)
             s = oracle.unit_select(A, wl.topk)
+            kp = oracle.bf16_to_f64(rows)
+            vp = kp[..., :wl.head_dim_v] if vrows is None else oracle.bf16_to_f64(vrows)
             keys = oracle.unit_selected_tokens(kp, s, n)
             vals = oracle.unit_selected_tokens(vp, s, n)
             oracle.unit_attention(qf, keys, vals, wl.scale)
             spent += time.perf_counter() - t0
-    per_unit = spent / len(picks)
-    step_s = per_unit * wl.batch * wl.num_kv_heads
+        done += 1
+    per_unit = spent / done
+    step_s = per_unit * len(units)
     return {"value": round(wl.batch / step_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{len(picks)} of {wl.batch * wl.num_kv_heads} (request, KV head) units of the same step, "
-                      f"fp64 numpy single-threaded, page bounds + KV-head max + top-k + attention given the page "
-                      f"summaries; {spent:.2f} s measured, scaled by units"}
+            "sample": f"{done} (request, KV head) units ({len(units)} make one decode step), fp64 numpy on one "
+                      f"thread: bf16 decoding of the unit's query and K/V pages, page bounds from the oracle's own page "
+                      f"summaries (built untimed), KV-head max, "
+                      f"top-k and attention; {spent:.1f} s measured, scaled by units to the step"}
 
 
 def torch_index(pages, phys, g):

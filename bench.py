@@ -52,13 +52,13 @@ def kernel_sources_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_record(kernel: str):
+def traffic_record(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 counters, if they were
-    taken on the current kernel sources (else None)."""
+    taken for this workload on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path)).get(kernel)
+    rec = json.load(open(path)).get(f"{kernel}@{workload}")
     if not rec or rec.get("sources_hash") != kernel_sources_hash():
         return None
     return rec.get("bytes_per_launch")
@@ -79,9 +79,12 @@ def main():
         return
 
     import sparse_kv_long_amd as se
-    from synth import WORKLOADS, make_quest_inputs
+    from synth import WORKLOADS, SnapKVWorkload, make_quest_inputs
 
     wl = WORKLOADS[args.workload]
+    if isinstance(wl, SnapKVWorkload):
+        bench_snapkv(args, wl)
+        return
     dev = "cuda"
     t0 = time.time()
     x = make_quest_inputs(wl, dev)
@@ -103,9 +106,7 @@ def main():
     # cache flush: READ 1 GiB (4x the Infinity Cache) so the caches fill with
     # clean lines; a write flush would leave dirty lines whose write-back
     # then competes with the measured kernel
-    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-    flush_sink = torch.empty((1,), dtype=torch.float32, device=dev)
-    flush = None if args.no_flush else (lambda: torch.sum(flush_buf, dim=(0,), keepdim=True, out=flush_sink))
+    flush = make_flush(torch, not args.no_flush)
     torch.cuda.synchronize()
 
     lens = x["seq_lens"].cpu().numpy().astype(np.int64)
@@ -128,25 +129,7 @@ def main():
         se.se_sparse_decode(L, P, q, x["k_pages"], x["v_pages"], x["page_table"], summ, x["seq_lens"], out, sel, ws)
 
     def timed(fn, count, warm):
-        for i in range(warm):
-            if flush:
-                flush()
-            fn(i)
-        torch.cuda.synchronize()
-        evs = []
-        wall0 = time.perf_counter()
-        for i in range(count):
-            if flush:
-                flush()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
-            fn(i)
-            b.record()
-            evs.append((a, b))
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - wall0
-        ms = np.array([a.elapsed_time(b) for a, b in evs])
-        return ms, wall
+        return timed_calls(fn, count, warm, flush)
 
     # whole step
     step_ms, wall = timed(step, args.steps, args.warmup)
@@ -175,7 +158,8 @@ def main():
     k34_gbps = bytes_k34 / t_k34 / 1e9
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if wl.name == "gqa32x4_d128_128k_b32" else
+        f"sparse decode tokens/s + effective HBM GB/s (% peak), {wl.name}, 1 GPU",
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -200,7 +184,7 @@ def main():
                       "decode_and_merge": round(float(np.mean(k34_ms)), 4)},
         "roofline": {"kernel": "quest_score (page scoring + last-page refresh)", "bound": "hbm",
                      "achieved": round(k1_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(k1_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_record("quest_score"),
+                     "frac": round(k1_gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_record("quest_score", wl.name),
                      "algorithmic_bytes_per_launch": bytes_k1},
         "decode_kernel_gbps": round(k34_gbps, 1),
         "input_generation_s": round(gen_s, 1),
@@ -209,6 +193,193 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, qs, args.cpu_seconds)
     print(json.dumps(result))
+
+
+def timed_calls(fn, count, warm, flush):
+    """Run fn(i) `warm` times, then `count` times each bracketed by HIP events
+    on the current stream (the one the library launches on); `flush` (if
+    any) runs before every call, outside the events."""
+    import numpy as np
+    import torch
+    for i in range(warm):
+        if flush:
+            flush()
+        fn(i)
+    torch.cuda.synchronize()
+    evs = []
+    wall0 = time.perf_counter()
+    for i in range(count):
+        if flush:
+            flush()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn(i)
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = np.array([a.elapsed_time(b) for a, b in evs])
+    return ms, wall
+
+
+def make_flush(torch, enabled):
+    """A 1 GiB read (4x the Infinity Cache): evicts the caches with clean lines
+    (a write flush would leave dirty lines whose write-back then competes
+    with the measured kernel)."""
+    if not enabled:
+        return None
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    flush_sink = torch.empty((1,), dtype=torch.float32, device="cuda")
+    return lambda: torch.sum(flush_buf, dim=(0,), keepdim=True, out=flush_sink)
+
+
+def bench_snapkv(args, wl):
+    """SnapKV eviction of a 32K-token prompt (window votes, pool, select,
+    compaction) followed by the decode steps over the compacted cache.  One
+    step = one eviction + all decode steps for the batch; tokens/s counts the
+    decode tokens produced.  The caches are flushed before the eviction only:
+    the compacted cache is small enough to stay in the Infinity Cache between
+    decode steps, as it would in serving."""
+    import numpy as np
+    import torch
+
+    import sparse_kv_long_amd as se
+    from synth import make_snapkv_inputs
+
+    dev = "cuda"
+    t0 = time.time()
+    x = make_snapkv_inputs(wl, dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    B, Hq, H, D, W, R, C = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window, wl.budget, wl.out_capacity
+    n = wl.prompt
+    p = se.snapkv_params(B, Hq, H, D, n, W, wl.pool_kernel, R, C, wl.scale)
+    ws = torch.empty(se.se_snapkv_workspace_size(p), dtype=torch.uint8, device=dev)
+    k_out = torch.zeros((B, H, C, D), dtype=torch.bfloat16, device=dev)
+    v_out = torch.zeros((B, H, C, D), dtype=torch.bfloat16, device=dev)
+    kept = torch.empty((B, H, R + W), dtype=torch.int32, device=dev)
+    klen = torch.empty((B, H), dtype=torch.int32, device=dev)
+    se.se_snapkv_compact(p, x["q_win"], x["k"], x["v"], x["prompt_lens"], k_out, v_out, kept, klen, ws)
+    torch.cuda.synchronize()
+    kl = int(klen[0, 0])
+    assert (klen == kl).all() and kl == R + W
+    # the decode steps' tokens go in at rows kl..kl+steps-1 (the engine's
+    # append); the eviction writes only rows < kept_len, so they are placed
+    # once, outside the timing
+    S = wl.decode_steps
+    k_out[:, :, kl:kl + S] = x["k_steps"].permute(1, 2, 0, 3)
+    v_out[:, :, kl:kl + S] = x["v_steps"].permute(1, 2, 0, 3)
+    MP = C // 16
+    pt = (torch.arange(B, device=dev)[:, None] * (H * MP) + torch.arange(MP, device=dev)[None]).to(torch.int32)
+    Ld = se.dense_layout(H, C, D)
+    Pd = se.decode_params(B, Hq, MP, MP, wl.scale)
+    wsd = torch.empty(se.se_sparse_decode_workspace_size(Ld, Pd), dtype=torch.uint8, device=dev)
+    out = torch.empty((S, B, Hq, D), dtype=torch.float32, device=dev)
+    lens = [torch.full((B,), kl + s + 1, dtype=torch.int32, device=dev) for s in range(S)]
+    flush = make_flush(torch, not args.no_flush)
+    torch.cuda.synchronize()
+
+    def evict(i):
+        se.se_snapkv_compact(p, x["q_win"], x["k"], x["v"], x["prompt_lens"], k_out, v_out, kept, klen, ws)
+
+    def decode_all(i):
+        for s in range(S):
+            se.se_sparse_decode(Ld, Pd, x["q_steps"][s], k_out, v_out, pt, None, lens[s], out[s], None, wsd)
+
+    def whole(i):
+        evict(i)
+        decode_all(i)
+
+    steps = max(1, args.steps // 5)
+    whole_ms, wall = timed_calls(whole, steps, 2, flush)
+    ev_ms, _ = timed_calls(evict, steps, 1, flush)
+    votes = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+    vo_ms, _ = timed_calls(lambda i: se.se_snapkv_votes(p, x["q_win"], x["k"], x["prompt_lens"], votes, ws), steps, 1,
+                           flush)
+    dec_ms, _ = timed_calls(decode_all, steps, 1, None)
+
+    t_whole = float(np.mean(whole_ms)) * 1e-3
+    tokens_s = B * S / t_whole
+    # algorithmic bytes: the window queries, K once, the kept K/V rows read and
+    # written, the kept ids; then per decode step the attended rows, q and out
+    rows_dec = sum(kl + s + 1 for s in range(S))
+    b_evict = B * Hq * W * D * 2 + B * H * n * D * 2 + 2 * 2 * B * H * kl * D * 2 + B * H * (R + W) * 4
+    b_dec = B * H * rows_dec * 2 * D * 2 + S * (B * Hq * D * 2 + B * Hq * D * 4)
+    b_votes = B * Hq * W * D * 2 + B * H * n * D * 2 + B * H * n * 4
+    flops_votes = 2 * 2 * B * Hq * W * n * D  # two passes over the window x context scores
+    t_votes = float(np.mean(vo_ms)) * 1e-3
+    t_ev = float(np.mean(ev_ms)) * 1e-3
+    t_dec = float(np.mean(dec_ms)) * 1e-3
+    result = {
+        "metric": "SnapKV eviction + decode tokens/s over the compacted cache, 32K prompt, 1 GPU",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": 2,
+        "ms_per_step": round(t_whole * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "prompt": n, "num_q_heads": Hq, "num_kv_heads": H,
+                   "head_dim": D, "window": W, "pool_kernel": wl.pool_kernel, "budget": R, "decode_steps": S},
+        "effective_hbm_gbps": round((b_evict + b_dec) / t_whole / 1e9, 1),
+        "algorithmic_bytes_per_step": b_evict + b_dec,
+        "pieces_ms": {"eviction": round(t_ev * 1e3, 4), "votes_only": round(t_votes * 1e3, 4),
+                      "decode_steps_total": round(t_dec * 1e3, 4), "decode_step_mean": round(t_dec * 1e3 / S, 5)},
+        "eviction_gbps": round(b_evict / t_ev / 1e9, 1),
+        "decode_gbps_cache_resident": round(b_dec / t_dec / 1e9, 1),
+        "roofline": {"kernel": "snapkv votes (row statistics + votes, MFMA)", "bound": "hbm",
+                     "achieved": round(b_votes / t_votes / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(b_votes / t_votes / 1e9 / HBM_PEAK_GBPS, 4), "traffic": traffic_record("snapkv_votes", wl.name),
+                     "algorithmic_bytes_per_launch": b_votes,
+                     "mfma_tflops": round(flops_votes / t_votes / 1e12, 1), "mfma_peak_tflops": 2500.0},
+        "cache_flush_before_eviction": flush is not None,
+        "wall_s_timed_loop_incl_flush": round(wall, 4),
+        "input_generation_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_snapkv(wl, x, args.cpu_seconds)
+    print(json.dumps(result))
+
+
+def cpu_baseline_snapkv(wl, x, seconds):
+    """The oracle's eviction (votes, pool, keep, row copies) and its decode
+    steps over the kept rows, per (request, KV head) unit on one thread, until
+    about `seconds` of CPU time are spent; scaled to the batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+    from synth import bf16_bits
+
+    G, W, R, S, n = wl.group, wl.window, wl.budget, wl.decode_steps, wl.prompt
+    units = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    order = np.random.default_rng(0).permutation(len(units))
+    spent, done = 0.0, 0
+    while spent < seconds and done < len(units):
+        b, g = units[int(order[done])]
+        qw = bf16_bits(x["q_win"][b, g * G:(g + 1) * G])
+        kb, vb = bf16_bits(x["k"][b, g]), bf16_bits(x["v"][b, g])
+        qs = bf16_bits(x["q_steps"][:, b, g * G:(g + 1) * G])
+        ks, vs = bf16_bits(x["k_steps"][:, b, g]), bf16_bits(x["v_steps"][:, b, g])
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            Sv, _, _ = oracle.snapkv_unit_votes(oracle.bf16_to_f64(qw), oracle.bf16_to_f64(kb), n, wl.scale)
+            keep = oracle.snapkv_unit_keep(oracle.maxpool1d(Sv, wl.pool_kernel), n, W, R)
+            kc = np.concatenate([kb[keep], ks])[None]
+            vc = np.concatenate([vb[keep], vs])[None]
+            for s in range(S):
+                oracle.decode_over_rows(qs[s], kc, vc, len(keep) + s + 1, G, wl.scale)
+            spent += time.perf_counter() - t0
+        done += 1
+    step_s = spent / done * len(units)
+    return {"value": round(wl.batch * S / step_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(units)} (request, KV head) units: fp64 numpy on one thread, votes over the "
+                      f"32K prompt, pool, keep, row copies and {S} decode steps each; {spent:.1f} s measured, "
+                      f"scaled by units to the batch"}
 
 
 def copy_calibration(torch):

@@ -289,18 +289,18 @@ __attribute__((amdgpu_waves_per_eu(DK <= 128 ? 4 : 2))) void decode_kernel(Decod
 //         token l%16, channels 8*(l/16) + 32*ks (16 bytes).  Exact bf16
 //         products, fp32 accumulation.
 //   p.v   O[h][c] = sum_t P[h][t] V[t][c], one page (16 tokens) per
-//         v_mfma_f32_16x16x16_bf16 k-step: value rows are loaded whole
-//         (lane l: tokens 4e + l/16, channels 8*(l%16)..+7), so a lane owns 8
-//         channels of 4 tokens; N-tile nt takes channels {8n + nt}, which
-//         makes every B-fragment a 2 x v_perm_b32 repack of the lane's own
-//         registers.
-//         P enters as a hi + lo pair of bf16 (P = hi + lo to ~2^-16), so the
-//         weights keep near-fp32 precision at two MFMAs per tile.
+//         v_mfma_f32_16x16x32_bf16: value rows are loaded whole (lane l:
+//         tokens 4e + l/16, channels 8*(l%16)..+7), so a lane owns 8 channels
+//         of 4 tokens; N-tile nt takes channels {8n + nt}, which makes every
+//         B-fragment a 2 x v_perm_b32 repack of the lane's own registers.
+//         P enters as a hi + lo pair of bf16 (P = hi + lo to ~2^-16): the
+//         32-wide k dimension holds the hi parts of the lane's 4 tokens, then
+//         their lo parts, against the same 4 value rows repeated, so the
+//         weights keep near-fp32 precision at one MFMA per tile.
 // Softmax, masking, the split partials and the merge are as in the VALU
 // kernel.
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const f32x4_t& c) {
@@ -322,10 +322,11 @@ struct MfmaDecodeShape {
 // loads of the next two pages in flight.  Lane l = 16*kq + col.
 //   q.k   A = K (lane: token col, channels 8kq + 32ks), B = q (head col);
 //         output lane (col, kq): tokens 4kq + i of the page, head col.
-//   p.v   A = P (lane: head col, tokens 4kq + e), B = V (lane: channels
-//         8col + nt, tokens 4kq + e) -- the weights stay in the lanes that
-//         computed them, and the value rows are loaded whole (16 lanes per
-//         256-byte row) and repacked in-lane with v_perm_b32.
+//   p.v   A = P (lane: head col, k 8kq + j = hi (j < 4) / lo (j >= 4) of
+//         token 4kq + j%4), B = V (lane: channels 8col + nt, the same tokens)
+//         -- the weights stay in the lanes that computed them, and the value
+//         rows are loaded whole (16 lanes per 256-byte row) and repacked
+//         in-lane with v_perm_b32.
 template <int G>
 __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts,
                                                          int pps, float scale2) {
@@ -439,8 +440,8 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
       hi[d] = (h0 >> 16) | h1;
       lo[d] = (l0 >> 16) | (l1 & 0xffff0000u);
     }
-    const bf16x4_t ph = __builtin_bit_cast(bf16x4_t, make_uint2(hi[0], hi[1]));
-    const bf16x4_t pl = __builtin_bit_cast(bf16x4_t, make_uint2(lo[0], lo[1]));
+    // k = 8kq + j: j < 4 the hi parts of tokens 4kq + j, j >= 4 the lo parts of the same tokens
+    const uint4 pa = make_uint4(hi[0], hi[1], lo[0], lo[1]);
     if (valid < kPage) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -451,9 +452,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
       const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
       const uint32_t f0 = __builtin_amdgcn_perm(dword(r.v[1], nt >> 1), dword(r.v[0], nt >> 1), sel);
       const uint32_t f1 = __builtin_amdgcn_perm(dword(r.v[3], nt >> 1), dword(r.v[2], nt >> 1), sel);
-      const bf16x4_t vf = __builtin_bit_cast(bf16x4_t, make_uint2(f0, f1));
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vf, acc[nt], 0, 0, 0);
-      acc[nt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vf, acc[nt], 0, 0, 0);
+      acc[nt] = mfma16(pa, make_uint4(f0, f1, f0, f1), acc[nt]);
     }
   };
 
@@ -513,6 +512,248 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core decode for the MLA layout: one 576-channel key row per token
+// (latent 512 + rope 64), the value is the first 512 channels of the same
+// row, and up to 32 query heads share it.
+//
+// One block of 4 waves per (split, KV head, request); all four waves walk the
+// same pages.  Wave w owns value channels [128w, 128w + 128): it loads those
+// 16 x 128 of each page once (lane: rows 4kq + e, channels 8col..+7), uses
+// them as the p.v operand, and, restaged through LDS in A-fragment order, for
+// its share of q.k (latent channels 128w.., plus rope channels 512 + 16w..).
+// The four partial logit tiles are summed through LDS in a fixed order, so
+// every wave holds the same logits, the same running max / sum and the same
+// weights; no merge across waves is needed at the end.  One block barrier
+// per page.
+// ---------------------------------------------------------------------------
+constexpr int kMlaPagesPerSplit = 512;
+constexpr int kMlaTargetBlocks = 256;
+
+template <int NHT>
+__global__ __launch_bounds__(256) void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts,
+                                                        int pps, float scale2) {
+  constexpr int DK = 576, DV = 512, NW = 4, PPS = kMlaPagesPerSplit;
+  __shared__ uint4 stage[NW][kPage * 16];     // per wave: 16 tokens x 16 chunks of 8 channels, swizzled
+  __shared__ f32x4_t sbuf[2][NW][NHT][kWave];  // partial logits, double-buffered over pages
+  __shared__ float alpha_lds[NW][NHT * 16];
+  __shared__ int64_t pid_lds[PPS];
+  __shared__ int vld_lds[PPS];
+
+  const int G = a.Hq / Hkv;
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int n = a.seq_lens[b];
+  const int P = (n + kPage - 1) / kPage;
+  const int32_t* list = nullptr;
+  const int32_t* plist = nullptr;
+  int kk = P;
+  if (a.selected) {
+    kk = min(a.topk, P);
+    list = a.selected + ((int64_t)b * Hkv + g) * a.topk;
+    if (a.selected_phys) plist = a.selected_phys + ((int64_t)b * Hkv + g) * a.topk;
+  }
+  const int p_begin = split * pps;
+  const int npg = max(0, min(p_begin + pps, kk) - p_begin);
+  const int nsplit = gridDim.x;
+  const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
+  if (npg == 0) {
+    for (int h = threadIdx.x; h < G; h += blockDim.x) {
+      a.part_ml[((head0 + h) * nsplit + split) * 2] = -__builtin_inff();
+      a.part_ml[((head0 + h) * nsplit + split) * 2 + 1] = 0.f;
+    }
+    return;
+  }
+  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
+    const int lp = list ? list[p_begin + i] : p_begin + i;
+    pid_lds[i] = plist ? plist[p_begin + i] : a.page_table[(int64_t)b * a.MP + lp];
+    vld_lds[i] = min(kPage, n - lp * kPage);
+  }
+  __syncthreads();
+
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const uint16_t* kb = a.k + (int64_t)g * hs;
+  const uint16_t* vrow = kb + 128 * w + 8 * col + (4 * kq) * ts;  // + e * ts: value rows 4kq + e
+  const uint16_t* rrow = kb + col * ts + 512 + 16 * w + 4 * kq;   // rope: token col, 4 channels
+
+  // q fragments: head 16ht + col; latent channels 128w + 32ks + 8kq, rope 512 + 16w + 4kq
+  uint4 qf[NHT][4];
+  uint2 qr[NHT];
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    const int h = 16 * ht + col;
+    const uint16_t* qh = a.q + (head0 + h) * DK;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ht][ks] = h < G ? ld16(qh + 128 * w + 32 * ks + 8 * kq) : make_uint4(0, 0, 0, 0);
+    qr[ht] = h < G ? *reinterpret_cast<const uint2*>(qh + 512 + 16 * w + 4 * kq) : make_uint2(0, 0);
+  }
+
+  struct PageRegs {
+    uint4 v[4];
+    uint2 r;
+  };
+  auto load = [&](int ii, PageRegs& R) {
+    const int64_t off = pid_lds[min(ii, npg - 1)] * ps;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) R.v[e] = ldnt16(vrow + off + e * ts);
+    R.r = *reinterpret_cast<const uint2*>(rrow + off);
+  };
+
+  float m_run[NHT], l_run[NHT];
+  f32x4_t acc[NHT][8];  // rows: heads 16ht + 4kq + i; columns: channels 128w + 8col + nt
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    m_run[ht] = -__builtin_inff();
+    l_run[ht] = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  uint4* st = stage[w];
+
+  auto page = [&](int ii, PageRegs& R) {
+    const int valid = vld_lds[ii];
+    const int buf = ii & 1;
+    // restage the wave's 16 x 128 slice as q.k A fragments (token col, channels 8kq + 32ks)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * kq + e;
+      st[t * 16 + (col ^ (t & 7))] = R.v[e];
+    }
+    __builtin_amdgcn_wave_barrier();  // lanes read what other lanes wrote
+    f32x4_t s[NHT];
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht)  // rope: k = 8kq + j, channels 512 + 16w + 4kq + j for j < 4, zero above
+      s[ht] = mfma16(make_uint4(R.r.x, R.r.y, 0u, 0u), make_uint4(qr[ht].x, qr[ht].y, 0u, 0u),
+                     f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 A = st[col * 16 + ((4 * ks + kq) ^ (col & 7))];
+#pragma unroll
+      for (int ht = 0; ht < NHT; ++ht) s[ht] = mfma16(A, qf[ht][ks], s[ht]);
+    }
+    __builtin_amdgcn_wave_barrier();  // the next page's restaging waits for these reads
+    // sum the four waves' channel shares (scaled to the log2 domain) in a fixed order
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      f32x4_t u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = s[ht][i] * scale2;
+      sbuf[buf][w][ht][lane] = u;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      f32x4_t t = sbuf[buf][0][ht][lane];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) {
+        const f32x4_t u = sbuf[buf][q][ht][lane];
+        t[0] += u[0];
+        t[1] += u[1];
+        t[2] += u[2];
+        t[3] += u[3];
+      }
+      s[ht] = t;
+    }
+    if (valid < kPage) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * kq + e >= valid) R.v[e] = make_uint4(0, 0, 0, 0);  // slots past the sequence may hold anything
+    }
+    uint32_t vfr[8][2];
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
+      vfr[nt][0] = __builtin_amdgcn_perm(dword(R.v[1], nt >> 1), dword(R.v[0], nt >> 1), sel);
+      vfr[nt][1] = __builtin_amdgcn_perm(dword(R.v[3], nt >> 1), dword(R.v[2], nt >> 1), sel);
+    }
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      const bool hv = 16 * ht + col < G;
+      float z[4];
+      float pm = -__builtin_inff();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        z[i] = (hv && 4 * kq + i < valid) ? s[ht][i] : -__builtin_inff();
+        pm = fmaxf(pm, z[i]);
+      }
+      pm = fmaxf(pm, __shfl_xor(pm, 16));
+      pm = fmaxf(pm, __shfl_xor(pm, 32));
+      const float m_new = fmaxf(m_run[ht], pm);
+      const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run[ht] - m_new);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
+      l_run[ht] = l_run[ht] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+      m_run[ht] = m_new;
+      if (__any(alpha != 1.f)) {
+        if (kq == 0) alpha_lds[w][16 * ht + col] = alpha;
+        __builtin_amdgcn_wave_barrier();
+        const float4 al = *reinterpret_cast<const float4*>(&alpha_lds[w][16 * ht + 4 * kq]);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          acc[ht][nt][0] *= al.x;
+          acc[ht][nt][1] *= al.y;
+          acc[ht][nt][2] *= al.z;
+          acc[ht][nt][3] *= al.w;
+        }
+        __builtin_amdgcn_wave_barrier();
+      }
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        const uint32_t h0 = __float_as_uint(p[2 * d]) & 0xffff0000u, h1 = __float_as_uint(p[2 * d + 1]) & 0xffff0000u;
+        const uint32_t l0 = __float_as_uint(p[2 * d] - __uint_as_float(h0));
+        const uint32_t l1 = __float_as_uint(p[2 * d + 1] - __uint_as_float(h1));
+        hi[d] = (h0 >> 16) | h1;
+        lo[d] = (l0 >> 16) | (l1 & 0xffff0000u);
+      }
+      const uint4 pa = make_uint4(hi[0], hi[1], lo[0], lo[1]);  // k = 8kq + j: hi (j < 4), lo (j >= 4)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        acc[ht][nt] = mfma16(pa, make_uint4(vfr[nt][0], vfr[nt][1], vfr[nt][0], vfr[nt][1]), acc[ht][nt]);
+    }
+  };
+
+  {
+    PageRegs r0, r1, r2;
+    load(0, r0);
+    load(1, r1);
+    for (int ii = 0; ii < npg; ii += 3) {
+      load(ii + 2, r2);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetches ahead of the compute
+      page(ii, r0);
+      load(ii + 3, r0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ii + 1 < npg) page(ii + 1, r1);
+      load(ii + 4, r1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ii + 2 < npg) page(ii + 2, r2);
+    }
+  }
+
+  // every wave holds the same (m, l); each writes its 128 channels of the split partial
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    float l = l_run[ht];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int hb = 16 * ht;
+    if (w == 0 && kq == 0 && hb + col < G) {
+      a.part_ml[((head0 + hb + col) * nsplit + split) * 2] = m_run[ht];
+      a.part_ml[((head0 + hb + col) * nsplit + split) * 2 + 1] = l;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = hb + 4 * kq + i;
+      if (h < G) {
+        float* dst = a.part_acc + ((head0 + h) * nsplit + split) * DV + 128 * w + 8 * col;
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[ht][0][i], acc[ht][1][i], acc[ht][2][i], acc[ht][3][i]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[ht][4][i], acc[ht][5][i], acc[ht][6][i], acc[ht][7][i]);
+      }
+    }
+  }
+}
+
 // One block per (request, query head).
 __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part_acc,
                                                     const float* __restrict__ part_ml, float* __restrict__ out,
@@ -540,8 +781,13 @@ static bool mfma_decode_shape(const Layout& L, int G) {
   return L.dk == 128 && L.dv == 128 && !L.visk && G <= 16 && use_mfma_decode();
 }
 
+static bool mla_decode_shape(const Layout& L, int G) {
+  return L.dk == 576 && L.dv == 512 && L.visk && G <= 32 && use_mfma_decode();
+}
+
 static int max_pps(const Layout& L, int G) {
   if (mfma_decode_shape(L, G)) return G <= 8 ? 64 : 32;
+  if (mla_decode_shape(L, G)) return kMlaPagesPerSplit;
   return (L.dk <= 128 && G <= 16) ? 32 : 16;
 }
 
@@ -555,7 +801,7 @@ int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, 
   // about one full round of resident blocks (256 CUs x 2 blocks of the
   // matrix-core kernel, x 4 of the VALU kernel): more splits only add per-block
   // latency and merge traffic (measured), a partial second round idles the chip
-  const int target = mfma_decode_shape(L, Hq / L.hkv) ? 512 : 1024;
+  const int target = mla_decode_shape(L, Hq / L.hkv) ? kMlaTargetBlocks : mfma_decode_shape(L, Hq / L.hkv) ? 512 : 1024;
   int s = requested > 0 ? requested : (target + units - 1) / units;
   if (s < smin) s = smin;
   if (s > kmax) s = kmax;
@@ -604,8 +850,20 @@ static hipError_t launch_mfma_g(const Layout& L, const DecodeArgs& a, int pps, h
   return hipGetLastError();
 }
 
-// Decode path: the matrix-core kernel for Dk = Dv = 128 and G <= 16 unless
-// SE_DECODE=valu; the VALU kernel for every other shape.
+template <int NHT>
+static hipError_t launch_mla(const Layout& L, const DecodeArgs& a, int pps, hipStream_t st) {
+  const float scale2 = a.scale * kLog2e;
+  dim3 grid(a.splits, L.hkv, a.B);
+  hipLaunchKernelGGL((decode_mla_kernel<NHT>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, pps, scale2);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, st, a.part_acc, a.part_ml, a.out, a.splits, 512);
+  return hipGetLastError();
+}
+
+// Decode path: the matrix-core kernels for Dk = Dv = 128 with G <= 16 and for
+// the MLA layout with G <= 32, unless SE_DECODE=valu; the VALU kernel for
+// every other shape.
 bool use_mfma_decode() {
   static const bool v = [] {
     const char* e = getenv("SE_DECODE");
@@ -630,6 +888,7 @@ hipError_t launch_decode(const Layout& L, const DecodeArgs& a, hipStream_t st) {
       default: break;
     }
   }
+  if (mla_decode_shape(L, G)) return G <= 16 ? launch_mla<1>(L, a, pps, st) : launch_mla<2>(L, a, pps, st);
   if (L.dk == 64 && L.dv == 64 && !L.visk) return launch_d<64, 64, false>(L, a, G, pps, st);
   if (L.dk == 128 && L.dv == 128 && !L.visk) return launch_d<128, 128, false>(L, a, G, pps, st);
   if (L.dk == 576 && L.dv == 512 && L.visk) return launch_d<576, 512, true>(L, a, G, pps, st);

@@ -105,4 +105,19 @@ __device__ __forceinline__ uint32_t float_key(float f) {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Copies src[0..n) (1 <= n <= N * blockDim.x) into LDS with all of a thread's
+// N loads issued before the first wait: a strided loop that stores each load
+// waits for that load before issuing the next.
+template <int N>
+__device__ __forceinline__ void stage_i32(const int32_t* __restrict__ src, int n, int32_t* dst) {
+  int32_t v[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) v[k] = src[min((int)threadIdx.x + k * (int)blockDim.x, n - 1)];
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const int i = threadIdx.x + k * blockDim.x;
+    if (i < n) dst[i] = v[k];
+  }
+}
+
 }  // namespace se

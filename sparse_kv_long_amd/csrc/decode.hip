@@ -376,7 +376,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
   uint4 qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    qf[ks] = col < G ? ld16(a.q + (head0 + col) * D + 8 * kq + 32 * ks) : make_uint4(0, 0, 0, 0);
+    qf[ks] = ld16(a.q + (head0 + min(col, G - 1)) * D + 8 * kq + 32 * ks);  // unconditional: loads issue together
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    if (col >= G) qf[ks] = make_uint4(0, 0, 0, 0);
 
   struct PageRegs {
     uint4 k[4], v[4];
@@ -582,10 +585,18 @@ __global__ __launch_bounds__(256) void decode_mla_kernel(DecodeArgs a, int Hkv, 
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
     const int h = 16 * ht + col;
-    const uint16_t* qh = a.q + (head0 + h) * DK;
+    const uint16_t* qh = a.q + (head0 + min(h, G - 1)) * DK;  // unconditional: the loads issue together
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qf[ht][ks] = h < G ? ld16(qh + 128 * w + 32 * ks + 8 * kq) : make_uint4(0, 0, 0, 0);
-    qr[ht] = h < G ? *reinterpret_cast<const uint2*>(qh + 512 + 16 * w + 4 * kq) : make_uint2(0, 0);
+    for (int ks = 0; ks < 4; ++ks) qf[ht][ks] = ld16(qh + 128 * w + 32 * ks + 8 * kq);
+    qr[ht] = *reinterpret_cast<const uint2*>(qh + 512 + 16 * w + 4 * kq);
+  }
+#pragma unroll
+  for (int ht = 0; ht < NHT; ++ht) {
+    if (16 * ht + col >= G) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qf[ht][ks] = make_uint4(0, 0, 0, 0);
+      qr[ht] = make_uint2(0, 0);
+    }
   }
 
   struct PageRegs {

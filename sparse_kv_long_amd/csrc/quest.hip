@@ -381,12 +381,14 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, const 
 
 // qq fragment of head h for k-chunk ci (8 elements): q- of channels 8ci.. for
 // ci < D/8, q+ of channels 8(ci - D/8).. otherwise; zero for h >= G.
+// The load is unconditional (clamped head) so that a run of these issues
+// back to back instead of waiting behind an exec-masked branch.
 __device__ __forceinline__ uint4 qq_chunk(const uint16_t* qrow_b, int h, int G, int D, int ci) {
-  if (h >= G) return make_uint4(0, 0, 0, 0);
   const int dc = D / 8;
   uint4 pos;
-  const uint4 neg = split_neg(ld16(qrow_b + (int64_t)h * D + 8 * (ci < dc ? ci : ci - dc)), pos);
-  return ci < dc ? neg : pos;
+  const uint4 neg = split_neg(ld16(qrow_b + (int64_t)min(h, G - 1) * D + 8 * (ci < dc ? ci : ci - dc)), pos);
+  const uint4 r = ci < dc ? neg : pos;
+  return h < G ? r : make_uint4(0, 0, 0, 0);
 }
 
 template <int D, int NT, bool BLDS, bool SUM>
@@ -413,8 +415,7 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
   const uint16_t* qrow_b = a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
   const int col = lane & 15, kq = lane >> 4;  // A: page slot / B: head; k-chunk quarter
 
-  if (!dense)
-    for (int i = threadIdx.x; i < blk_end - blk_start; i += blockDim.x) ids[i] = ptrow[blk_start + i];
+  if (!dense) stage_i32<4 * kMaxPagesPerWave / 256>(ptrow + blk_start, blk_end - blk_start, ids);
   if constexpr (BLDS) {
     for (int i = threadIdx.x; i < NT * KS * 64; i += blockDim.x) {
       const int l = i & 63, ks = (i >> 6) % KS, nt = (i >> 6) / KS;
@@ -574,10 +575,180 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
   }
 }
 
+// ---------------------------------------------------------------------------
+// K1 for wide records (the 576-channel MLA key: a 2304-byte record per page).
+// A block streams 16-page tiles: its 256 threads fetch a tile's records as
+// whole contiguous runs (consecutive threads take consecutive 16-byte chunks
+// of a record), write them to an LDS tile with chunk c of page p stored at
+// slot c ^ (p & 7), and the four waves then split the tile's k dimension
+// (wave w: k-steps 9w..9w+8 of 36), reading their A fragments from LDS
+// without bank conflicts and keeping their q+/q- fragments in registers.
+// The partial tiles are summed through LDS in a fixed order and wave w
+// finishes rows i = w (pages 4*kq + w of the tile).
+// ---------------------------------------------------------------------------
+constexpr int kWidePagesPerBlock = 2048;
+
+template <int D, int NT>
+__global__ __launch_bounds__(256) void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs,
+                                                               int64_t ts, int ppb) {
+  constexpr int KS = 2 * D / 32;  // k steps per tile
+  constexpr int KW = KS / 4;      // k steps per wave
+  constexpr int NCH = D / 4;      // 16-byte chunks per record
+  constexpr int CPT = 16 * NCH / 256;  // chunks per thread per tile
+  static_assert(KS % 4 == 0 && (16 * NCH) % 256 == 0 && NCH % 8 == 0, "unsupported record width");
+  __shared__ int32_t ids[kWidePagesPerBlock];
+  __shared__ uint4 tile[2][16 * NCH];
+  __shared__ f32x4_t part[2][4][NT][kWave];
+  __shared__ uint4 rrec[NCH];
+
+  const int b = blockIdx.z, g = blockIdx.y;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  const int n = a.seq_lens[b];
+  const int P = (n + kPage - 1) / kPage;
+  const bool dense = a.topk >= P;
+  const int start = blockIdx.x * ppb;
+  if (start >= P) return;
+  int end = min(start + ppb, P);
+  const int plast = P - 1;
+  const bool do_refresh = a.refresh && plast < end;
+  if (dense && !do_refresh) return;
+  if (a.refresh) end = min(end, plast);
+  const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
+  const uint16_t* qrow_b = a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
+  const bool SUM = a.head_sum != 0;
+  float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
+
+  if (!dense && end > start) stage_i32<kWidePagesPerBlock / 256>(ptrow + start, end - start, ids);
+  // this wave's q-/q+ fragments: head 16nt + col, k-chunk kq + 4*(KW*wave + ks)
+  uint4 qb[NT][KW];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < KW; ++ks) qb[nt][ks] = qq_chunk(qrow_b, nt * 16 + col, G, D, kq + 4 * (KW * wave + ks));
+  __syncthreads();
+
+  // partial tiles -> KV-head scores of pages base + 4*kq + wave (lanes col == 0 store)
+  auto finish = [&](const f32x4_t (&s)[NT], int buf, int base, int lim) {
+    // scaled on the vector ALU before the LDS store (the store never reads an
+    // accumulator straight out of the matrix core)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4_t u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u[i] = s[nt][i] * a.scale;
+      part[buf][wave][nt][lane] = u;
+    }
+    __syncthreads();
+    float v = 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float x = part[buf][0][nt][lane][wave];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) x += part[buf][w][nt][lane][wave];
+      const bool real = nt * 16 + col < G;
+      x = real ? x : (SUM ? 0.f : -__builtin_inff());
+      v = nt == 0 ? x : (SUM ? v + x : fmaxf(v, x));
+    }
+    v = SUM ? group_sum<16>(v) : group_max_any<16>(v);
+    const int p = base + 4 * kq + wave;
+    if (col == 0 && p < lim) srow[p] = v;
+  };
+
+  const uint16_t* summ_g = a.summ + (int64_t)g * 2 * D;
+  const int64_t pid_stride = (int64_t)Hkv * 2 * D;
+  int buf = 0;
+  if (!dense && start < end) {
+    const int npg = end - start;
+    const int ntile = (npg + 15) / 16;
+    uint4 rA[CPT], rB[CPT];
+    // chunk u = r*256 + tid of the tile: page u / NCH, chunk u % NCH
+    auto load = [&](int t, uint4 (&r)[CPT]) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int u = c * 256 + threadIdx.x;
+        const int p = min(16 * t + u / NCH, npg - 1);
+        r[c] = ldnt16(summ_g + (int64_t)ids[p] * pid_stride + 8 * (u % NCH));
+      }
+    };
+    auto stage = [&](int tb, const uint4 (&r)[CPT]) {
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) {
+        const int u = c * 256 + threadIdx.x;
+        const int pg = u / NCH, ch = u % NCH;
+        tile[tb][pg * NCH + (ch ^ (pg & 7))] = r[c];
+      }
+    };
+    auto score = [&](int t) {
+      const int tb = t & 1;
+      f32x4_t s[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) s[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KW; ++ks) {
+        const int ch = kq + 4 * (KW * wave + ks);
+        const uint4 av = tile[tb][col * NCH + (ch ^ (col & 7))];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) s[nt] = mfma16(av, qb[nt][ks], s[nt]);
+      }
+      finish(s, buf, start + 16 * t, end);
+      buf ^= 1;
+    };
+    load(0, rA);
+    load(min(1, ntile - 1), rB);
+    for (int t = 0; t < ntile; t += 2) {
+      stage(0, rA);
+      __syncthreads();
+      load(min(t + 2, ntile - 1), rA);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+      score(t);
+      if (t + 1 < ntile) {
+        stage(1, rB);
+        __syncthreads();
+        load(min(t + 3, ntile - 1), rB);
+        __builtin_amdgcn_sched_barrier(0);
+        score(t + 1);
+      }
+    }
+  }
+
+  if (do_refresh) {
+    // rebuild the last page's summary from its valid keys, store it, score it
+    const int64_t pid = ptrow[plast];
+    const int valid = n - plast * kPage;
+    const int dc = D / 8;
+    uint16_t* rec = a.summ + (pid * Hkv + g) * 2 * D;
+    for (int ci = threadIdx.x; ci < NCH; ci += blockDim.x) {
+      uint4 mn, mx;
+      minmax8(a.k + pid * ps + (int64_t)g * hs + 8 * (ci < dc ? ci : ci - dc), ts, valid, mn, mx);
+      const uint4 v = ci < dc ? mn : mx;
+      *reinterpret_cast<uint4*>(rec + 8 * ci) = v;
+      rrec[ci] = v;
+    }
+    __syncthreads();
+    if (!dense) {
+      f32x4_t s[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        s[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KW; ++ks) {
+          const uint4 d = col == 0 ? rrec[kq + 4 * (KW * wave + ks)] : make_uint4(0, 0, 0, 0);
+          s[nt] = mfma16(d, qb[nt][ks], s[nt]);
+        }
+      }
+      finish(s, buf, plast, plast + 1);  // page slot 0 of the tile is the last page
+    }
+  }
+}
+
 static int pick_ppw(int B, int Hkv, int MP) {
-  // about 2048 waves (8 per CU); between 32 and kMaxPagesPerWave pages each
+  // about 3072 waves: 768 blocks, the three per CU that the matrix-core
+  // kernel's LDS allows, all resident at once (measured: fewer waves leave
+  // HBM idle, a second round of blocks costs more than it hides); between 32
+  // and kMaxPagesPerWave pages each
   const int64_t pages = (int64_t)B * Hkv * MP;
-  int64_t ppw = (pages + 2047) / 2048;
+  int64_t ppw = (pages + 3071) / 3072;
   ppw = (ppw + 31) / 32 * 32;
   if (ppw < 32) ppw = 32;
   if (ppw > kMaxPagesPerWave) ppw = kMaxPagesPerWave;
@@ -631,6 +802,20 @@ static hipError_t launch_mfma(const Layout& L, const ScoreArgs& a, int G, hipStr
   return hipGetLastError();
 }
 
+template <int D, int NT>
+static hipError_t launch_wide(const Layout& L, const ScoreArgs& a, int G, hipStream_t st) {
+  // whole tiles; at most kWidePagesPerBlock pages per block
+  const int64_t pages = (int64_t)a.B * L.hkv * a.MP;
+  int64_t ppb = (pages + 255) / 256;  // one block per CU (the LDS tile allows no more)
+  ppb = (ppb + 15) / 16 * 16;
+  if (ppb < 16) ppb = 16;
+  if (ppb > kWidePagesPerBlock) ppb = kWidePagesPerBlock;
+  dim3 grid((unsigned)((a.MP + ppb - 1) / ppb), L.hkv, a.B);
+  hipLaunchKernelGGL((quest_score_wide_kernel<D, NT>), grid, dim3(256), 0, st, a, G, L.hkv, L.ps, L.hs, L.ts,
+                     (int)ppb);
+  return hipGetLastError();
+}
+
 // Scoring path: the matrix-core kernel unless SE_QUEST_SCORE=valu selects
 // the VALU kernels (kept for comparison).
 static bool use_valu_scoring() {
@@ -647,7 +832,7 @@ hipError_t launch_quest_scores(const Layout& L, const ScoreArgs& a, hipStream_t 
   if (!use_valu_scoring()) {
     if (L.dk == 64) return G <= 16 ? launch_mfma<64, 1, false>(L, a, G, st) : launch_mfma<64, 2, false>(L, a, G, st);
     if (L.dk == 128) return G <= 16 ? launch_mfma<128, 1, false>(L, a, G, st) : launch_mfma<128, 2, false>(L, a, G, st);
-    if (L.dk == 576) return G <= 16 ? launch_mfma<576, 1, true>(L, a, G, st) : launch_mfma<576, 2, true>(L, a, G, st);
+    if (L.dk == 576) return G <= 16 ? launch_wide<576, 1>(L, a, G, st) : launch_wide<576, 2>(L, a, G, st);
     return hipErrorInvalidValue;
   }
 #define SE_REG(GG, DD) \

@@ -335,6 +335,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
   __shared__ float comb[NW * G * D];
   __shared__ float wml[NW][G][2];
   __shared__ float alpha_lds[NW][16];
+  __shared__ uint4 kstage[NW][kPage * 16];  // per wave: 16 tokens x 16 chunks of 8 channels, swizzled
   __shared__ int64_t pid_lds[PPS];
   __shared__ int vld_lds[PPS];
 
@@ -370,8 +371,11 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
   const int npw = npg > w ? (npg - w + NW - 1) / NW : 0;  // pages of this wave: w + NW*ii
-  const uint16_t* kg = a.k + (int64_t)g * hs + col * ts + 8 * kq;
+  // K and V rows are both loaded whole (lane: rows 4kq + e, channels 8col..+7);
+  // K is restaged through this wave's LDS tile into the q.k A layout
+  const uint16_t* kg = a.k + (int64_t)g * hs + 8 * col + (4 * kq) * ts;
   const uint16_t* vg = a.v + (int64_t)g * hs + 8 * col;
+  uint4* st = kstage[w];
 
   uint4 qf[4];
 #pragma unroll
@@ -387,7 +391,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
   auto load = [&](int ii, PageRegs& r) {
     const int64_t off = pid_lds[w + NW * min(ii, npw - 1)] * ps;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) r.k[ks] = ldnt16(kg + off + 32 * ks);
+    for (int e = 0; e < 4; ++e) r.k[e] = ldnt16(kg + off + e * ts);
 #pragma unroll
     for (int e = 0; e < 4; ++e) r.v[e] = ldnt16(vg + off + (4 * kq + e) * ts);
   };
@@ -400,9 +404,16 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
 
   auto page = [&](int ii, PageRegs& r) {
     const int valid = vld_lds[w + NW * ii];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 4 * kq + e;
+      st[t * 16 + (col ^ (t & 7))] = r.k[e];
+    }
+    __builtin_amdgcn_wave_barrier();  // lanes read what other lanes wrote
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) s = mfma16(r.k[ks], qf[ks], s);
+    for (int ks = 0; ks < 4; ++ks) s = mfma16(st[col * 16 + ((4 * ks + kq) ^ (col & 7))], qf[ks], s);
+    __builtin_amdgcn_wave_barrier();  // the next page's restaging waits for these reads
     float z[4];
     float pm = -__builtin_inff();
 #pragma unroll

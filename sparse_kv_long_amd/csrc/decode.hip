@@ -544,9 +544,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
 constexpr int kMlaPagesPerSplit = 512;
 constexpr int kMlaTargetBlocks = 256;
 
-template <int NHT>
-__global__ __launch_bounds__(256) void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts,
-                                                        int pps, float scale2) {
+template <int NHT, int RD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts, int pps, float scale2) {
   constexpr int DK = 576, DV = 512, NW = 4, PPS = kMlaPagesPerSplit;
   __shared__ uint4 stage[NW][kPage * 16];     // per wave: 16 tokens x 16 chunks of 8 channels, swizzled
   __shared__ f32x4_t sbuf[2][NW][NHT][kWave];  // partial logits, double-buffered over pages
@@ -737,19 +737,18 @@ __global__ __launch_bounds__(256) void decode_mla_kernel(DecodeArgs a, int Hkv, 
   };
 
   {
-    PageRegs r0, r1, r2;
-    load(0, r0);
-    load(1, r1);
-    for (int ii = 0; ii < npg; ii += 3) {
-      load(ii + 2, r2);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetches ahead of the compute
-      page(ii, r0);
-      load(ii + 3, r0);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ii + 1 < npg) page(ii + 1, r1);
-      load(ii + 4, r1);
-      __builtin_amdgcn_sched_barrier(0);
-      if (ii + 2 < npg) page(ii + 2, r2);
+    // RD pages in the register ring (RD - 1 in flight while one is consumed):
+    // the block is alone on its CU, so deep prefetch is what keeps HBM busy
+    PageRegs r[RD];
+#pragma unroll
+    for (int j = 0; j < RD - 1; ++j) load(j, r[j]);
+    for (int ii = 0; ii < npg; ii += RD) {
+#pragma unroll
+      for (int j = 0; j < RD; ++j) {
+        load(ii + j + RD - 1, r[(j + RD - 1) % RD]);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetches ahead of the compute
+        if (j == 0 || ii + j < npg) page(ii + j, r[j]);
+      }
     }
   }
 
@@ -776,24 +775,49 @@ __global__ __launch_bounds__(256) void decode_mla_kernel(DecodeArgs a, int Hkv, 
   }
 }
 
-// One block per (request, query head).
-__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part_acc,
+// One block per (request, query head).  One wave turns the splits' (m, l)
+// into weights w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s' (0 for an empty
+// split) in LDS; then every thread sums w_s acc_s for its channels with all
+// loads unconditional, so they are issued back to back.
+constexpr int kMaxSplits = 1024;
+
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_acc,
                                                     const float* __restrict__ part_ml, float* __restrict__ out,
                                                     int nsplit, int DV) {
+  __shared__ float wts[kMaxSplits];
   const int64_t bh = blockIdx.x;
   const float* ml = part_ml + bh * nsplit * 2;
-  float M = -__builtin_inff();
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ml[2 * s]);
-  float den = 0.f;
-  for (int s = 0; s < nsplit; ++s)
-    if (ml[2 * s] != -__builtin_inff()) den += __builtin_amdgcn_exp2f(ml[2 * s] - M) * ml[2 * s + 1];
-  const float inv = den > 0.f ? 1.f / den : 0.f;
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    float M = -__builtin_inff();
+    for (int sp = lane; sp < nsplit; sp += kWave) M = fmaxf(M, ml[2 * sp]);
+    M = wave_max(M);
+    float den = 0.f;
+    for (int sp = lane; sp < nsplit; sp += kWave) {
+      const float m = ml[2 * sp];
+      den += m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M) * ml[2 * sp + 1];
+    }
+    den = wave_sum(den);
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    for (int sp = lane; sp < nsplit; sp += kWave) {
+      const float m = ml[2 * sp];
+      wts[sp] = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - M) * inv;
+    }
+  }
+  __syncthreads();
+  // an empty split never wrote its acc: its weight is 0 and its acc is not used
+  auto term = [&](int sp, float a) { return wts[sp] != 0.f ? wts[sp] * a : 0.f; };
+  const float* acc = part_acc + bh * nsplit * DV;
   for (int c = threadIdx.x; c < DV; c += blockDim.x) {
     float num = 0.f;
-    for (int s = 0; s < nsplit; ++s)
-      if (ml[2 * s] != -__builtin_inff())
-        num += __builtin_amdgcn_exp2f(ml[2 * s] - M) * part_acc[(bh * nsplit + s) * DV + c];
-    out[bh * DV + c] = num * inv;
+    int sp = 0;
+    for (; sp + 4 <= nsplit; sp += 4) {
+      const float a0 = acc[(int64_t)sp * DV + c], a1 = acc[(int64_t)(sp + 1) * DV + c];
+      const float a2 = acc[(int64_t)(sp + 2) * DV + c], a3 = acc[(int64_t)(sp + 3) * DV + c];
+      num += (term(sp, a0) + term(sp + 1, a1)) + (term(sp + 2, a2) + term(sp + 3, a3));
+    }
+    for (; sp < nsplit; ++sp) num += term(sp, acc[(int64_t)sp * DV + c]);
+    out[bh * DV + c] = num;
   }
 }
 
@@ -827,6 +851,7 @@ int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, 
   int s = requested > 0 ? requested : (target + units - 1) / units;
   if (s < smin) s = smin;
   if (s > kmax) s = kmax;
+  if (s > kMaxSplits) s = kMaxSplits;
   const int pps = (kmax + s - 1) / s;
   return (kmax + pps - 1) / pps;
 }
@@ -876,7 +901,7 @@ template <int NHT>
 static hipError_t launch_mla(const Layout& L, const DecodeArgs& a, int pps, hipStream_t st) {
   const float scale2 = a.scale * kLog2e;
   dim3 grid(a.splits, L.hkv, a.B);
-  hipLaunchKernelGGL((decode_mla_kernel<NHT>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, pps, scale2);
+  hipLaunchKernelGGL((decode_mla_kernel<NHT, 3>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, pps, scale2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, st, a.part_acc, a.part_ml, a.out, a.splits, 512);

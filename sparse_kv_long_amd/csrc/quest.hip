@@ -588,9 +588,9 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
 // ---------------------------------------------------------------------------
 constexpr int kWidePagesPerBlock = 2048;
 
-template <int D, int NT>
-__global__ __launch_bounds__(256) void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs,
-                                                               int64_t ts, int ppb) {
+template <int D, int NT, int RD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs, int64_t ts, int ppb) {
   constexpr int KS = 2 * D / 32;  // k steps per tile
   constexpr int KW = KS / 4;      // k steps per wave
   constexpr int NCH = D / 4;      // 16-byte chunks per record
@@ -661,8 +661,7 @@ __global__ __launch_bounds__(256) void quest_score_wide_kernel(ScoreArgs a, int 
   if (!dense && start < end) {
     const int npg = end - start;
     const int ntile = (npg + 15) / 16;
-    uint4 rA[CPT], rB[CPT];
-    // chunk u = r*256 + tid of the tile: page u / NCH, chunk u % NCH
+    // chunk u = c*256 + tid of the tile: page u / NCH, chunk u % NCH
     auto load = [&](int t, uint4 (&r)[CPT]) {
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
@@ -694,20 +693,21 @@ __global__ __launch_bounds__(256) void quest_score_wide_kernel(ScoreArgs a, int 
       finish(s, buf, start + 16 * t, end);
       buf ^= 1;
     };
-    load(0, rA);
-    load(min(1, ntile - 1), rB);
-    for (int t = 0; t < ntile; t += 2) {
-      stage(0, rA);
-      __syncthreads();
-      load(min(t + 2, ntile - 1), rA);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-      score(t);
-      if (t + 1 < ntile) {
-        stage(1, rB);
-        __syncthreads();
-        load(min(t + 3, ntile - 1), rB);
-        __builtin_amdgcn_sched_barrier(0);
-        score(t + 1);
+    // RD tiles in the register ring: RD - 1 in flight while one is staged and
+    // scored (the block is alone on its CU, so deep prefetch keeps HBM busy)
+    uint4 r[RD][CPT];
+#pragma unroll
+    for (int j = 0; j < RD - 1; ++j) load(min(j, ntile - 1), r[j]);
+    for (int t = 0; t < ntile; t += RD) {
+#pragma unroll
+      for (int j = 0; j < RD; ++j) {
+        if (j == 0 || t + j < ntile) {
+          stage((t + j) & 1, r[j]);
+          __syncthreads();
+          load(min(t + j + RD - 1, ntile - 1), r[(j + RD - 1) % RD]);
+          __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+          score(t + j);
+        }
       }
     }
   }
@@ -811,7 +811,7 @@ static hipError_t launch_wide(const Layout& L, const ScoreArgs& a, int G, hipStr
   if (ppb < 16) ppb = 16;
   if (ppb > kWidePagesPerBlock) ppb = kWidePagesPerBlock;
   dim3 grid((unsigned)((a.MP + ppb - 1) / ppb), L.hkv, a.B);
-  hipLaunchKernelGGL((quest_score_wide_kernel<D, NT>), grid, dim3(256), 0, st, a, G, L.hkv, L.ps, L.hs, L.ts,
+  hipLaunchKernelGGL((quest_score_wide_kernel<D, NT, 2>), grid, dim3(256), 0, st, a, G, L.hkv, L.ps, L.hs, L.ts,
                      (int)ppb);
   return hipGetLastError();
 }

@@ -361,22 +361,9 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
     }
     return;
   }
-  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
-    const int lp = list ? list[p_begin + i] : p_begin + i;
-    pid_lds[i] = plist ? plist[p_begin + i] : a.page_table[(int64_t)b * a.MP + lp];
-    vld_lds[i] = min(kPage, n - lp * kPage);
-  }
-  __syncthreads();
-
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
-  const int npw = npg > w ? (npg - w + NW - 1) / NW : 0;  // pages of this wave: w + NW*ii
-  // K and V rows are both loaded whole (lane: rows 4kq + e, channels 8col..+7);
-  // K is restaged through this wave's LDS tile into the q.k A layout
-  const uint16_t* kg = a.k + (int64_t)g * hs + 8 * col + (4 * kq) * ts;
-  const uint16_t* vg = a.v + (int64_t)g * hs + 8 * col;
-  uint4* st = kstage[w];
-
+  // q fragments first: independent of the page ids, so both loads overlap
   uint4 qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
@@ -384,16 +371,38 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     if (col >= G) qf[ks] = make_uint4(0, 0, 0, 0);
+  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
+    const int lp = list ? list[p_begin + i] : p_begin + i;
+    pid_lds[i] = plist ? plist[p_begin + i] : a.page_table[(int64_t)b * a.MP + lp];
+    vld_lds[i] = min(kPage, n - lp * kPage);
+  }
+  __syncthreads();
+
+  const int npw = npg > w ? (npg - w + NW - 1) / NW : 0;  // pages of this wave: w + NW*ii
+  // K and V rows are both loaded whole (lane: rows 4kq + e, channels 8col..+7);
+  // K is restaged through this wave's LDS tile into the q.k A layout
+  uint4* st = kstage[w];
+
 
   struct PageRegs {
     uint4 k[4], v[4];
   };
+  // the page base is wave-uniform (scalar registers); each lane adds the same
+  // 32-bit byte offsets for K and V rows
+  uint32_t roff[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) roff[e] = (uint32_t)(2 * (8 * col + (4 * kq + e) * ts));
+  const uint16_t* kh = a.k + (int64_t)g * hs;
+  const uint16_t* vh = a.v + (int64_t)g * hs;
   auto load = [&](int ii, PageRegs& r) {
-    const int64_t off = pid_lds[w + NW * min(ii, npw - 1)] * ps;
+    const int64_t pid = pid_lds[w + NW * min(ii, npw - 1)];
+    const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane((int)pid) * ps;
+    const char* kp = reinterpret_cast<const char*>(kh + off);
+    const char* vp = reinterpret_cast<const char*>(vh + off);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r.k[e] = ldnt16(kg + off + e * ts);
+    for (int e = 0; e < 4; ++e) r.k[e] = ldnt16(kp + roff[e]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r.v[e] = ldnt16(vg + off + (4 * kq + e) * ts);
+    for (int e = 0; e < 4; ++e) r.v[e] = ldnt16(vp + roff[e]);
   };
 
   float m_run = -__builtin_inff();  // running max of head col (log2 domain)

@@ -23,8 +23,11 @@ namespace se {
 
 constexpr int kTopkThreads = 1024;
 
+constexpr int kRadixBits = 11;                // digit width of a descent pass
+constexpr int kRadixBins = 1 << kRadixBits;   // 2048 bins: two or three passes resolve fp32 scores
+
 struct TopkShared {
-  uint32_t hist[256];
+  uint32_t hist[2][kRadixBins];  // alternate passes: one is counted while the other is cleared
   int wave_tot[2][kTopkThreads / kWave];
   uint32_t wave_and[kTopkThreads / kWave], wave_or[kTopkThreads / kWave];
   int digit, above, done;
@@ -94,7 +97,8 @@ __device__ __forceinline__ void block_and_or(uint32_t& vand, uint32_t& vor, Topk
 // Requires 0 < k < N <= KPT * 1024.  Writes k indices into out[0..k) and,
 // when `translate` is given, translate[index] into out2[0..k).
 template <int KPT>
-__device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t* __restrict__ out, TopkShared& sm,
+__device__ __forceinline__ void block_topk(const float* __restrict__ row, int N, int k, int32_t* __restrict__ out,
+                                           TopkShared& sm,
                            const int32_t* __restrict__ translate = nullptr, int32_t* __restrict__ out2 = nullptr) {
   const int tid = threadIdx.x;
   const int base = tid * KPT;
@@ -128,50 +132,63 @@ __device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t*
     }
   }
   if (tid == 0) sm.done = 0;
+  for (int i = tid; i < kRadixBins; i += kTopkThreads) sm.hist[0][i] = 0;
   // bits above the highest bit where the keys differ are common to all keys;
   // the radix passes start below them (scores of one magnitude share their
   // top byte, which would otherwise funnel every key into one bin)
-  block_and_or(kand, kor, sm);
+  block_and_or(kand, kor, sm);  // its barrier also publishes the cleared histogram
   const uint32_t diff = kand ^ kor;
   uint32_t prefix = diff ? (kand & ~(0xffffffffu >> __builtin_clz(diff))) : kand;
   uint32_t pmask = diff ? ~(0xffffffffu >> __builtin_clz(diff)) : 0xffffffffu;
   int rem = k;
   int hi = diff ? 31 - __builtin_clz(diff) : -1;
+  int hb = 0;
   // Descend until the threshold bin is resolved: either every bit is fixed
   // (ties broken by index below), or the bin holds exactly the `rem` keys
-  // still needed, in which case every key of the bin is taken.
+  // still needed, in which case every key of the bin is taken.  Two barriers
+  // per pass: after the counting, and after the scan (during which the other
+  // waves clear the next pass's histogram).
 #pragma unroll 1
   while (hi >= 0) {
-    const int lo = hi >= 7 ? hi - 7 : 0;
+    const int lo = hi >= kRadixBits - 1 ? hi - (kRadixBits - 1) : 0;
     const uint32_t dmask = (1u << (hi - lo + 1)) - 1u;
-    if (tid < 256) sm.hist[tid] = 0;
-    __syncthreads();
+    uint32_t* H = sm.hist[hb];
 #pragma unroll
     for (int i = 0; i < KPT; ++i)
-      if (base + i < N && (key[i] & pmask) == prefix) atomicAdd(&sm.hist[(key[i] >> lo) & dmask], 1u);
+      if (base + i < N && (key[i] & pmask) == prefix) atomicAdd(&H[(key[i] >> lo) & dmask], 1u);
     __syncthreads();
-    if (tid < 64) {
-      const int c0 = sm.hist[4 * tid], c1 = sm.hist[4 * tid + 1], c2 = sm.hist[4 * tid + 2], c3 = sm.hist[4 * tid + 3];
-      const int local = c0 + c1 + c2 + c3;
+    if (tid < kWave) {
+      // lane t owns bins BPL*t .. BPL*t + BPL-1; only the lane whose range holds
+      // the threshold walks its bins a second time
+      constexpr int BPL = kRadixBins / kWave;
+      const uint4* h4 = reinterpret_cast<const uint4*>(&H[BPL * tid]);
+      int local = 0;
+#pragma unroll
+      for (int r = 0; r < BPL / 4; ++r) {
+        const uint4 v = h4[r];
+        local += (int)(v.x + v.y + v.z + v.w);
+      }
       const int incl = wave_incl_scan(local);
       const int total = __builtin_amdgcn_readlane(incl, 63);
-      const int above = total - incl;  // bins >= 4*tid + 4
-      const int s3 = above + c3, s2 = s3 + c2, s1 = s2 + c1, s0 = s1 + c0;
-      int d = -1, ab = 0, cnt = 0;
-      if (above < rem && s3 >= rem) {
-        d = 4 * tid + 3, ab = above, cnt = c3;
-      } else if (s3 < rem && s2 >= rem) {
-        d = 4 * tid + 2, ab = s3, cnt = c2;
-      } else if (s2 < rem && s1 >= rem) {
-        d = 4 * tid + 1, ab = s2, cnt = c1;
-      } else if (s1 < rem && s0 >= rem) {
-        d = 4 * tid, ab = s1, cnt = c0;
-      }
-      if (d >= 0) {
+      int above = total - incl;  // keys in bins >= BPL * (tid + 1)
+      if (above < rem && above + local >= rem) {
+        int d = BPL * tid, cnt = 0;
+        for (int j = BPL - 1; j >= 0; --j) {
+          const int cj = (int)H[BPL * tid + j];
+          if (above + cj >= rem) {
+            d = BPL * tid + j;
+            cnt = cj;
+            break;
+          }
+          above += cj;
+        }
         sm.digit = d;
-        sm.above = ab;
-        sm.done = (cnt == rem - ab) ? 1 : 0;
+        sm.above = above;
+        sm.done = (cnt == rem - above) ? 1 : 0;
       }
+    } else {
+      uint32_t* Hn = sm.hist[hb ^ 1];
+      for (int i = tid - kWave; i < kRadixBins; i += kTopkThreads - kWave) Hn[i] = 0;
     }
     __syncthreads();
     prefix |= (uint32_t)sm.digit << lo;
@@ -179,6 +196,7 @@ __device__ void block_topk(const float* __restrict__ row, int N, int k, int32_t*
     rem -= sm.above;
     if (sm.done) break;
     hi = lo - 1;
+    hb ^= 1;
   }
   // selection: (key & pmask) > prefix, or == prefix among the first `rem` such
   // keys by index (all of them when the descent stopped early)

@@ -86,7 +86,7 @@ def test_scores_and_last_page_refresh(name, head_agg):
 
 
 @pytest.mark.parametrize("MP,topk", [(5, 2), (300, 17), (1024, 64), (3000, 256), (9000, 300), (20000, 2048),
-                                     (40000, 1000)])
+                                     (40000, 1000), (65536, 4096)])
 def test_topk_pages_exact(MP, topk):
     announce(f"topk MP {MP} topk {topk}")
     rng = np.random.default_rng(MP + topk)
@@ -204,3 +204,33 @@ def test_empty_and_single_token_requests():
     ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], sel_lists(to_np(sel), h["lens"]),
                                   wl.group, wl.scale, wl.head_dim_v)
     check_attention(o, ref, 8.0, "edge")
+
+
+def test_longest_supported_request():
+    """One request at the largest page table the library takes (65536 pages,
+    about 1M tokens, the last page partial), through the whole decode step."""
+    wl = QuestWorkload("t_1m", 1, 8, 1, 128, 128, 65536 * 16, 512, "zipf", seed=23)
+    n = 65536 * 16 - 5
+    announce(f"longest request n {n}")
+    x = make_quest_inputs(wl, DEV, poison_tail=True, seq_lens=[n])
+    summ = build_summaries(x, wl)
+    out, sel = run_sparse_decode(x, wl, summ)
+    pt = to_np(x["page_table"])
+    Pb = -(-n // 16)
+    kbits = bf16_bits(x["k_pages"].index_select(0, torch.from_numpy(pt[0, :Pb].astype(np.int64)).to(DEV))[:, 0])
+    kp = oracle.gather_unit_pages(kbits[:, None], np.arange(Pb), 0, n)
+    mins, maxs = oracle.unit_summaries(kp, n)
+    qf = oracle.bf16_to_f64(bf16_bits(x["q"])[0])
+    A = oracle.unit_kv_head_score(oracle.unit_page_bounds(qf, mins, maxs, wl.scale))
+    S = to_np(sel)
+    check_selection(S[0, 0], A, wl.topk, "1M")
+    chosen = S[0, 0].astype(np.int64)
+    vbits = bf16_bits(x["v_pages"].index_select(0, torch.from_numpy(pt[0, chosen].astype(np.int64)).to(DEV))[:, 0])
+    keys = oracle.unit_selected_tokens(kp, chosen, n)
+    vp = np.full((Pb, 16, 128), np.nan)
+    vp[chosen] = oracle.gather_unit_pages(vbits[:, None], np.arange(len(chosen)), 0, len(chosen) * 16)
+    if chosen[-1] == Pb - 1:  # the partial last page keeps only its valid rows
+        vp[Pb - 1, n - (Pb - 1) * 16:] = np.nan
+    vals = oracle.unit_selected_tokens(vp, chosen, n)
+    ref = oracle.unit_attention(qf, keys, vals, wl.scale)
+    check_attention(to_np(out)[0], ref, float(np.abs(vals).max()), "1M")

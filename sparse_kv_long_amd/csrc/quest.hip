@@ -366,7 +366,7 @@ __global__ __launch_bounds__(256) void quest_score_lds_kernel(ScoreArgs a, int G
 // page l%16 and k-chunk l/16 (+4 per k step) of the record, i.e. 16-byte
 // loads that form 64-byte contiguous runs; the output element i of lane l is
 // page 4*(l/16)+i, head l%16, so the KV-head max (or sum) is a 16-lane DPP
-// reduction.  qq fragments sit in registers (D <= 128) or in LDS (D = 576).
+// reduction.  qq fragments sit in registers.
 // The wave that owns a request's last page rebuilds that page's summary from
 // its keys with all 64 lanes (each lane one 16-byte chunk: min or max of 8
 // channels over the valid tokens), stores it, and scores it from LDS.
@@ -391,16 +391,14 @@ __device__ __forceinline__ uint4 qq_chunk(const uint16_t* qrow_b, int h, int G, 
   return h < G ? r : make_uint4(0, 0, 0, 0);
 }
 
-template <int D, int NT, bool BLDS, bool SUM>
+template <int D, int NT, bool SUM>
 __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs,
                                                                int64_t ts, int ppw) {
   constexpr int KS = 2 * D / 32;  // k steps per 16-page tile
   constexpr int NCH = D / 4;      // 16-byte chunks per record
-  constexpr bool STAGE = D <= 128;  // records staged through LDS in the 8-lanes-per-record shape
-  extern __shared__ uint4 dyn_lds[];  // BLDS: qq fragments [NT][KS][64]
   __shared__ int32_t ids[4 * kMaxPagesPerWave];
   __shared__ uint4 refresh_rec[4][NCH];
-  __shared__ uint4 stage_lds[STAGE ? 4 * 16 * NCH : 1];
+  __shared__ uint4 stage_lds[4 * 16 * NCH];
 
   const int b = blockIdx.z, g = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -416,12 +414,6 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
   const int col = lane & 15, kq = lane >> 4;  // A: page slot / B: head; k-chunk quarter
 
   if (!dense) stage_i32<4 * kMaxPagesPerWave / 256>(ptrow + blk_start, blk_end - blk_start, ids);
-  if constexpr (BLDS) {
-    for (int i = threadIdx.x; i < NT * KS * 64; i += blockDim.x) {
-      const int l = i & 63, ks = (i >> 6) % KS, nt = (i >> 6) / KS;
-      dyn_lds[i] = qq_chunk(qrow_b, nt * 16 + (l & 15), G, D, (l >> 4) + 4 * ks);
-    }
-  }
   __syncthreads();
 
   const int start = blk_start + wave * ppw;
@@ -431,20 +423,14 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
   if (dense && !do_refresh) return;
   if (a.refresh) end = min(end, plast);
 
-  uint4 qb[BLDS ? 1 : NT][BLDS ? 1 : KS];
-  if constexpr (!BLDS) {
+  uint4 qb[NT][KS];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+  for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qb[nt][ks] = qq_chunk(qrow_b, nt * 16 + col, G, D, kq + 4 * ks);
-  }
-  auto bfrag = [&](int nt, int ks) -> uint4 {
-    if constexpr (BLDS) return dyn_lds[(nt * KS + ks) * 64 + lane];
-    else return qb[nt][ks];
-  };
+    for (int ks = 0; ks < KS; ++ks) qb[nt][ks] = qq_chunk(qrow_b, nt * 16 + col, G, D, kq + 4 * ks);
+  auto bfrag = [&](int nt, int ks) -> uint4 { return qb[nt][ks]; };
 
   const uint16_t* summ_g0 = a.summ + (int64_t)g * 2 * D;
-  const uint16_t* summ_g = summ_g0 + 8 * kq;
   const int64_t pid_stride = (int64_t)Hkv * 2 * D;
   float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
 
@@ -468,81 +454,52 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
 
   if (!dense && start < end) {
     const int ntile = (end - start + 15) / 16;
-    if constexpr (STAGE) {
-      // Records are fetched 8 lanes per record (one full 128-byte line per
-      // lane group and instruction: lane l takes record l/8 of each half tile
-      // and chunks l%8 + 8c), written to this wave's LDS tile with chunk ci of
-      // page p stored at slot ci ^ p, and read back in the MFMA A layout, which
-      // the swizzle makes bank-conflict free.
-      constexpr int CPR = NCH / 8;  // chunks per lane per record
-      uint4* tile = stage_lds + wave * 16 * NCH;
-      const int r8 = lane >> 3, j8 = lane & 7;
-      uint4 dA[2][CPR], dB[2][CPR];
-      auto load = [&](int t, uint4 (&d)[2][CPR]) {
+    // Records are fetched 8 lanes per record (one full 128-byte line per
+    // lane group and instruction: lane l takes record l/8 of each half tile
+    // and chunks l%8 + 8c), written to this wave's LDS tile with chunk ci of
+    // page p stored at slot ci ^ p, and read back in the MFMA A layout, which
+    // the swizzle makes bank-conflict free.
+    constexpr int CPR = NCH / 8;  // chunks per lane per record
+    uint4* tile = stage_lds + wave * 16 * NCH;
+    const int r8 = lane >> 3, j8 = lane & 7;
+    uint4 dA[2][CPR], dB[2][CPR];
+    auto load = [&](int t, uint4 (&d)[2][CPR]) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int p = min(start + 16 * t + 8 * u + r8, end - 1);
-          const uint16_t* rec = summ_g0 + (int64_t)ids[p - blk_start] * pid_stride + 8 * j8;
+      for (int u = 0; u < 2; ++u) {
+        const int p = min(start + 16 * t + 8 * u + r8, end - 1);
+        const uint16_t* rec = summ_g0 + (int64_t)ids[p - blk_start] * pid_stride + 8 * j8;
 #pragma unroll
-          for (int c = 0; c < CPR; ++c) d[u][c] = ldnt16(rec + 64 * c);
-        }
-      };
-      auto score = [&](int t, const uint4 (&d)[2][CPR]) {
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int pg = 8 * u + r8;
-#pragma unroll
-          for (int c = 0; c < CPR; ++c) tile[pg * NCH + ((j8 + 8 * c) ^ pg)] = d[u][c];
-        }
-        __builtin_amdgcn_wave_barrier();
-        f32x4_t acc[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 av = tile[col * NCH + ((kq + 4 * ks) ^ col)];
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(av, bfrag(nt, ks), acc[nt]);
-        }
-        __builtin_amdgcn_wave_barrier();
-        finish(acc, start + 16 * t, end);
-      };
-      load(0, dA);
-      for (int t = 0; t < ntile; t += 2) {
-        load(min(t + 1, ntile - 1), dB);
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-        score(t, dA);
-        load(min(t + 2, ntile - 1), dA);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t + 1 < ntile) score(t + 1, dB);
+        for (int c = 0; c < CPR; ++c) d[u][c] = ldnt16(rec + 64 * c);
       }
-    } else {
-      uint4 dA[KS], dB[KS];
-      auto load = [&](int t, uint4 (&d)[KS]) {
-        const int p = min(start + 16 * t + col, end - 1);
-        const uint16_t* rec = summ_g + (int64_t)ids[p - blk_start] * pid_stride;
+    };
+    auto score = [&](int t, const uint4 (&d)[2][CPR]) {
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) d[ks] = ldnt16(rec + 32 * ks);
-      };
-      auto score = [&](int t, const uint4 (&d)[KS]) {
-        f32x4_t acc[NT];
+      for (int u = 0; u < 2; ++u) {
+        const int pg = 8 * u + r8;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) acc[nt] = mfma16(d[ks], bfrag(nt, ks), acc[nt]);
-        }
-        finish(acc, start + 16 * t, end);
-      };
-      load(0, dA);
-      for (int t = 0; t < ntile; t += 2) {
-        load(min(t + 1, ntile - 1), dB);
-        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-        score(t, dA);
-        load(min(t + 2, ntile - 1), dA);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t + 1 < ntile) score(t + 1, dB);
+        for (int c = 0; c < CPR; ++c) tile[pg * NCH + ((j8 + 8 * c) ^ pg)] = d[u][c];
       }
+      __builtin_amdgcn_wave_barrier();
+      f32x4_t acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 av = tile[col * NCH + ((kq + 4 * ks) ^ col)];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma16(av, bfrag(nt, ks), acc[nt]);
+      }
+      __builtin_amdgcn_wave_barrier();
+      finish(acc, start + 16 * t, end);
+    };
+    load(0, dA);
+    for (int t = 0; t < ntile; t += 2) {
+      load(min(t + 1, ntile - 1), dB);
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+      score(t, dA);
+      load(min(t + 2, ntile - 1), dA);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t + 1 < ntile) score(t + 1, dB);
     }
   }
 
@@ -780,25 +737,16 @@ static hipError_t launch_lds(const Layout& L, const ScoreArgs& a, int G, hipStre
   return hipGetLastError();
 }
 
-template <int D, int NT, bool BLDS>
+template <int D, int NT>
 static hipError_t launch_mfma(const Layout& L, const ScoreArgs& a, int G, hipStream_t st) {
   const int ppw = pick_ppw(a.B, L.hkv, a.MP);
   dim3 grid((a.MP + 4 * ppw - 1) / (4 * ppw), L.hkv, a.B);
-  const size_t lds = BLDS ? (size_t)NT * (2 * D / 32) * 64 * sizeof(uint4) : 0;
-  if (lds > 65536) {
-    hipError_t e = hipFuncSetAttribute((const void*)quest_score_mfma_kernel<D, NT, BLDS, false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)quest_score_mfma_kernel<D, NT, BLDS, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
   if (a.head_sum)
-    hipLaunchKernelGGL((quest_score_mfma_kernel<D, NT, BLDS, true>), grid, dim3(256), lds, st, a, G, L.hkv, L.ps, L.hs,
-                       L.ts, ppw);
+    hipLaunchKernelGGL((quest_score_mfma_kernel<D, NT, true>), grid, dim3(256), 0, st, a, G, L.hkv, L.ps, L.hs, L.ts,
+                       ppw);
   else
-    hipLaunchKernelGGL((quest_score_mfma_kernel<D, NT, BLDS, false>), grid, dim3(256), lds, st, a, G, L.hkv, L.ps,
-                       L.hs, L.ts, ppw);
+    hipLaunchKernelGGL((quest_score_mfma_kernel<D, NT, false>), grid, dim3(256), 0, st, a, G, L.hkv, L.ps, L.hs, L.ts,
+                       ppw);
   return hipGetLastError();
 }
 
@@ -830,8 +778,8 @@ hipError_t launch_quest_scores(const Layout& L, const ScoreArgs& a, hipStream_t 
   const int G = a.Hq / L.hkv;
   if (a.B == 0 || a.MP == 0) return hipSuccess;
   if (!use_valu_scoring()) {
-    if (L.dk == 64) return G <= 16 ? launch_mfma<64, 1, false>(L, a, G, st) : launch_mfma<64, 2, false>(L, a, G, st);
-    if (L.dk == 128) return G <= 16 ? launch_mfma<128, 1, false>(L, a, G, st) : launch_mfma<128, 2, false>(L, a, G, st);
+    if (L.dk == 64) return G <= 16 ? launch_mfma<64, 1>(L, a, G, st) : launch_mfma<64, 2>(L, a, G, st);
+    if (L.dk == 128) return G <= 16 ? launch_mfma<128, 1>(L, a, G, st) : launch_mfma<128, 2>(L, a, G, st);
     if (L.dk == 576) return G <= 16 ? launch_wide<576, 1>(L, a, G, st) : launch_wide<576, 2>(L, a, G, st);
     return hipErrorInvalidValue;
   }

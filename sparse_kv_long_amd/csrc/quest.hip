@@ -534,59 +534,79 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
 
 // ---------------------------------------------------------------------------
 // K1 for wide records (the 576-channel MLA key: a 2304-byte record per page).
-// A block streams 16-page tiles: its 256 threads fetch a tile's records as
-// whole contiguous runs (consecutive threads take consecutive 16-byte chunks
-// of a record), write them to an LDS tile with chunk c of page p stored at
-// slot c ^ (p & 7), and the four waves then split the tile's k dimension
-// (wave w: k-steps 9w..9w+8 of 36), reading their A fragments from LDS
-// without bank conflicts and keeping their q+/q- fragments in registers.
-// The partial tiles are summed through LDS in a fixed order and wave w
-// finishes rows i = w (pages 4*kq + w of the tile).
+//
+// Work balance: the pages to score of all (request, KV head) units form one
+// sequence (unit-major); block i takes the i-th of gridDim.x equal shares, as
+// segments of one or more units, so a ragged batch keeps every block equally
+// busy.  The last page of each unit, whose summary is rebuilt first, is
+// handled by block (unit mod gridDim.x) after its share.
+//
+// Within a segment the block streams 16-page tiles: its threads fetch a
+// tile's records as contiguous runs (consecutive threads take consecutive
+// 16-byte chunks of a record) into registers, RD tiles deep, and write the
+// current one to an LDS tile with chunk c of page p stored at slot c ^ (p & 7).
+// The NW waves split the tile's k dimension (wave w: k-steps KW*w .. KW*w +
+// KW-1), reading their A fragments from LDS without bank conflicts and keeping
+// their q+/q- fragments in registers.  The partial tiles are summed through
+// LDS in a fixed order and waves 0..3 finish rows i = w (pages 4*kq + w of the
+// tile).  Twelve waves of three k-steps each keep the registers per wave small
+// enough for a deep ring, which is what keeps HBM busy with one block per CU.
 // ---------------------------------------------------------------------------
-constexpr int kWidePagesPerBlock = 2048;
+constexpr int kWideChunk = 2048;     // page ids staged per pass over a segment
+constexpr int kWideWaves = 12;
+constexpr int kWideMaxUnits = 4096;  // units per launch (prefix sums live in LDS)
 
 template <int D, int NT, int RD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs, int64_t ts, int ppb) {
+__global__ __launch_bounds__(kWideWaves * 64)
+void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs, int64_t ts, int u0, int nunits) {
+  constexpr int NW = kWideWaves, NTH = NW * 64;
   constexpr int KS = 2 * D / 32;  // k steps per tile
-  constexpr int KW = KS / 4;      // k steps per wave
+  constexpr int KW = KS / NW;     // k steps per wave
   constexpr int NCH = D / 4;      // 16-byte chunks per record
-  constexpr int CPT = 16 * NCH / 256;  // chunks per thread per tile
-  static_assert(KS % 4 == 0 && (16 * NCH) % 256 == 0 && NCH % 8 == 0, "unsupported record width");
-  __shared__ int32_t ids[kWidePagesPerBlock];
-  __shared__ uint4 tile[2][16 * NCH];
-  __shared__ f32x4_t part[2][4][NT][kWave];
+  constexpr int CPT = 16 * NCH / NTH;  // chunks per thread per tile
+  static_assert(KS % NW == 0 && (16 * NCH) % NTH == 0 && NCH % 8 == 0, "unsupported record width");
+  __shared__ int32_t ids[kWideChunk];
+  __shared__ uint4 tile[16 * NCH];
+  __shared__ f32x4_t part[2][NW][NT][kWave];
   __shared__ uint4 rrec[NCH];
+  __shared__ int64_t pre[kWideMaxUnits + 1];  // pages to score before each unit
 
-  const int b = blockIdx.z, g = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
-  const int n = a.seq_lens[b];
-  const int P = (n + kPage - 1) / kPage;
-  const bool dense = a.topk >= P;
-  const int start = blockIdx.x * ppb;
-  if (start >= P) return;
-  int end = min(start + ppb, P);
-  const int plast = P - 1;
-  const bool do_refresh = a.refresh && plast < end;
-  if (dense && !do_refresh) return;
-  if (a.refresh) end = min(end, plast);
-  const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
-  const uint16_t* qrow_b = a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
   const bool SUM = a.head_sum != 0;
-  float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
+  const int64_t pid_stride = (int64_t)Hkv * 2 * D;
 
-  if (!dense && end > start) stage_i32<kWidePagesPerBlock / 256>(ptrow + start, end - start, ids);
-  // this wave's q-/q+ fragments: head 16nt + col, k-chunk kq + 4*(KW*wave + ks)
-  uint4 qb[NT][KW];
+  // pages to score per unit (dense units score none; the refreshed last page
+  // is scored separately) and their prefix sums, by the first wave
+  auto scored = [&](int u) -> int {
+    const int b = (u0 + u) / Hkv;
+    const int P = (a.seq_lens[b] + kPage - 1) / kPage;
+    if (a.topk >= P) return 0;
+    return a.refresh ? P - 1 : P;
+  };
+  if (wave == 0) {
+    int64_t carry = 0;
+    for (int c0 = 0; c0 < nunits; c0 += kWave) {
+      const int u = c0 + lane;
+      const int v = u < nunits ? scored(u) : 0;
+      int x = v;
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int ks = 0; ks < KW; ++ks) qb[nt][ks] = qq_chunk(qrow_b, nt * 16 + col, G, D, kq + 4 * (KW * wave + ks));
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+      }
+      if (u < nunits) pre[u] = carry + x - v;
+      carry += __shfl(x, kWave - 1);
+    }
+    if (lane == 0) pre[nunits] = carry;
+  }
   __syncthreads();
+  const int64_t total = pre[nunits];
+  const int64_t lo = total * blockIdx.x / gridDim.x, hi = total * (blockIdx.x + 1) / gridDim.x;
 
-  // partial tiles -> KV-head scores of pages base + 4*kq + wave (lanes col == 0 store)
-  auto finish = [&](const f32x4_t (&s)[NT], int buf, int base, int lim) {
+  // partial tiles -> KV-head scores of pages base + 4*kq + wave (waves 0..3,
+  // lanes col == 0 store)
+  auto finish = [&](const f32x4_t (&s)[NT], int buf, float* srow, int base, int lim) {
     // scaled on the vector ALU before the LDS store (the store never reads an
     // accumulator straight out of the matrix core)
 #pragma unroll
@@ -597,85 +617,115 @@ void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs
       part[buf][wave][nt][lane] = u;
     }
     __syncthreads();
-    float v = 0.f;
+    if (wave < 4) {
+      float v = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      float x = part[buf][0][nt][lane][wave];
+      for (int nt = 0; nt < NT; ++nt) {
+        float x = part[buf][0][nt][lane][wave];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) x += part[buf][w][nt][lane][wave];
-      const bool real = nt * 16 + col < G;
-      x = real ? x : (SUM ? 0.f : -__builtin_inff());
-      v = nt == 0 ? x : (SUM ? v + x : fmaxf(v, x));
+        for (int w = 1; w < NW; ++w) x += part[buf][w][nt][lane][wave];
+        const bool real = nt * 16 + col < G;
+        x = real ? x : (SUM ? 0.f : -__builtin_inff());
+        v = nt == 0 ? x : (SUM ? v + x : fmaxf(v, x));
+      }
+      v = SUM ? group_sum<16>(v) : group_max_any<16>(v);
+      const int p = base + 4 * kq + wave;
+      if (col == 0 && p < lim) srow[p] = v;
     }
-    v = SUM ? group_sum<16>(v) : group_max_any<16>(v);
-    const int p = base + 4 * kq + wave;
-    if (col == 0 && p < lim) srow[p] = v;
+  };
+  // this wave's q-/q+ fragments for unit (b, g): head 16nt + col, k-chunk kq + 4*(KW*wave + ks)
+  uint4 qb[NT][KW];
+  auto load_q = [&](int b, int g) {
+    const uint16_t* qrow_b = a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < KW; ++ks) qb[nt][ks] = qq_chunk(qrow_b, nt * 16 + col, G, D, kq + 4 * (KW * wave + ks));
   };
 
-  const uint16_t* summ_g = a.summ + (int64_t)g * 2 * D;
-  const int64_t pid_stride = (int64_t)Hkv * 2 * D;
   int buf = 0;
-  if (!dense && start < end) {
-    const int npg = end - start;
-    const int ntile = (npg + 15) / 16;
-    // chunk u = c*256 + tid of the tile: page u / NCH, chunk u % NCH
-    auto load = [&](int t, uint4 (&r)[CPT]) {
+  // ---- this block's share, unit by unit ---------------------------------------
+  int u = 0;
+  while (u < nunits && pre[u + 1] <= lo) ++u;
+  for (; u < nunits && pre[u] < hi; ++u) {
+    const int64_t s0 = max(lo, pre[u]) - pre[u], s1 = min(hi, pre[u + 1]) - pre[u];
+    if (s1 <= s0) continue;
+    const int b = (u0 + u) / Hkv, g = (u0 + u) % Hkv;
+    load_q(b, g);
+    const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
+    float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
+    const uint16_t* summ_g = a.summ + (int64_t)g * 2 * D;
+    for (int c0 = (int)s0; c0 < (int)s1; c0 += kWideChunk) {
+      const int npg = min(kWideChunk, (int)s1 - c0);
+      __syncthreads();  // the previous chunk's ids are no longer read
+      stage_i32<(kWideChunk + NTH - 1) / NTH>(ptrow + c0, npg, ids);
+      __syncthreads();
+      const int ntile = (npg + 15) / 16;
+      auto load = [&](int t, uint4 (&r)[CPT]) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int u = c * 256 + threadIdx.x;
-        const int p = min(16 * t + u / NCH, npg - 1);
-        r[c] = ldnt16(summ_g + (int64_t)ids[p] * pid_stride + 8 * (u % NCH));
-      }
-    };
-    auto stage = [&](int tb, const uint4 (&r)[CPT]) {
+        for (int c = 0; c < CPT; ++c) {
+          const int uu = c * NTH + threadIdx.x;
+          const int p = min(16 * t + uu / NCH, npg - 1);
+          r[c] = ldnt16(summ_g + (int64_t)ids[p] * pid_stride + 8 * (uu % NCH));
+        }
+      };
+      // one LDS tile: the previous tile's fragment reads all precede the
+      // barrier inside its finish, so the next tile may overwrite it
+      auto stage = [&](const uint4 (&r)[CPT]) {
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) {
-        const int u = c * 256 + threadIdx.x;
-        const int pg = u / NCH, ch = u % NCH;
-        tile[tb][pg * NCH + (ch ^ (pg & 7))] = r[c];
-      }
-    };
-    auto score = [&](int t) {
-      const int tb = t & 1;
-      f32x4_t s[NT];
+        for (int c = 0; c < CPT; ++c) {
+          const int uu = c * NTH + threadIdx.x;
+          const int pg = uu / NCH, ch = uu % NCH;
+          tile[pg * NCH + (ch ^ (pg & 7))] = r[c];
+        }
+      };
+      auto score = [&](int t) {
+        f32x4_t sc[NT];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) s[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NT; ++nt) sc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KW; ++ks) {
-        const int ch = kq + 4 * (KW * wave + ks);
-        const uint4 av = tile[tb][col * NCH + (ch ^ (col & 7))];
+        for (int ks = 0; ks < KW; ++ks) {
+          const int ch = kq + 4 * (KW * wave + ks);
+          const uint4 av = tile[col * NCH + (ch ^ (col & 7))];
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) s[nt] = mfma16(av, qb[nt][ks], s[nt]);
-      }
-      finish(s, buf, start + 16 * t, end);
-      buf ^= 1;
-    };
-    // RD tiles in the register ring: RD - 1 in flight while one is staged and
-    // scored (the block is alone on its CU, so deep prefetch keeps HBM busy)
-    uint4 r[RD][CPT];
+          for (int nt = 0; nt < NT; ++nt) sc[nt] = mfma16(av, qb[nt][ks], sc[nt]);
+        }
+        finish(sc, buf, srow, c0 + 16 * t, c0 + npg);
+        buf ^= 1;
+      };
+      // RD tiles in the register ring: RD - 1 in flight while one is staged and scored
+      uint4 r[RD][CPT];
 #pragma unroll
-    for (int j = 0; j < RD - 1; ++j) load(min(j, ntile - 1), r[j]);
-    for (int t = 0; t < ntile; t += RD) {
+      for (int j = 0; j < RD - 1; ++j) load(min(j, ntile - 1), r[j]);
+      for (int t = 0; t < ntile; t += RD) {
 #pragma unroll
-      for (int j = 0; j < RD; ++j) {
-        if (j == 0 || t + j < ntile) {
-          stage((t + j) & 1, r[j]);
-          __syncthreads();
-          load(min(t + j + RD - 1, ntile - 1), r[(j + RD - 1) % RD]);
-          __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-          score(t + j);
+        for (int j = 0; j < RD; ++j) {
+          if (j == 0 || t + j < ntile) {
+            stage(r[j]);
+            __syncthreads();
+            load(min(t + j + RD - 1, ntile - 1), r[(j + RD - 1) % RD]);
+            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+            score(t + j);
+          }
         }
       }
     }
   }
 
-  if (do_refresh) {
-    // rebuild the last page's summary from its valid keys, store it, score it
-    const int64_t pid = ptrow[plast];
+  // ---- last pages: rebuild each summary from its valid keys, store it, score it
+  if (!a.refresh) return;
+  for (int ur = blockIdx.x; ur < nunits; ur += gridDim.x) {
+    const int b = (u0 + ur) / Hkv, g = (u0 + ur) % Hkv;
+    const int n = a.seq_lens[b];
+    const int P = (n + kPage - 1) / kPage;
+    if (P == 0) continue;
+    const int plast = P - 1;
+    const int64_t pid = a.page_table[(int64_t)b * a.MP + plast];
     const int valid = n - plast * kPage;
     const int dc = D / 8;
     uint16_t* rec = a.summ + (pid * Hkv + g) * 2 * D;
-    for (int ci = threadIdx.x; ci < NCH; ci += blockDim.x) {
+    __syncthreads();  // rrec of the previous unit is no longer read
+    for (int ci = threadIdx.x; ci < NCH; ci += NTH) {
       uint4 mn, mx;
       minmax8(a.k + pid * ps + (int64_t)g * hs + 8 * (ci < dc ? ci : ci - dc), ts, valid, mn, mx);
       const uint4 v = ci < dc ? mn : mx;
@@ -683,18 +733,20 @@ void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs
       rrec[ci] = v;
     }
     __syncthreads();
-    if (!dense) {
-      f32x4_t s[NT];
+    if (a.topk < P) {
+      load_q(b, g);
+      f32x4_t sc[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
-        s[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        sc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KW; ++ks) {
           const uint4 d = col == 0 ? rrec[kq + 4 * (KW * wave + ks)] : make_uint4(0, 0, 0, 0);
-          s[nt] = mfma16(d, qb[nt][ks], s[nt]);
+          sc[nt] = mfma16(d, qb[nt][ks], sc[nt]);
         }
       }
-      finish(s, buf, plast, plast + 1);  // page slot 0 of the tile is the last page
+      finish(sc, buf, a.scores + ((int64_t)b * Hkv + g) * a.MP, plast, plast + 1);  // page slot 0 is the last page
+      buf ^= 1;
     }
   }
 }
@@ -752,16 +804,16 @@ static hipError_t launch_mfma(const Layout& L, const ScoreArgs& a, int G, hipStr
 
 template <int D, int NT>
 static hipError_t launch_wide(const Layout& L, const ScoreArgs& a, int G, hipStream_t st) {
-  // whole tiles; at most kWidePagesPerBlock pages per block
-  const int64_t pages = (int64_t)a.B * L.hkv * a.MP;
-  int64_t ppb = (pages + 255) / 256;  // one block per CU (the LDS tile allows no more)
-  ppb = (ppb + 15) / 16 * 16;
-  if (ppb < 16) ppb = 16;
-  if (ppb > kWidePagesPerBlock) ppb = kWidePagesPerBlock;
-  dim3 grid((unsigned)((a.MP + ppb - 1) / ppb), L.hkv, a.B);
-  hipLaunchKernelGGL((quest_score_wide_kernel<D, NT, 2>), grid, dim3(256), 0, st, a, G, L.hkv, L.ps, L.hs, L.ts,
-                     (int)ppb);
-  return hipGetLastError();
+  // one block per CU (its LDS allows no more); units in launches of at most kWideMaxUnits
+  const int units = a.B * L.hkv;
+  for (int u0 = 0; u0 < units; u0 += kWideMaxUnits) {
+    const int nu = units - u0 < kWideMaxUnits ? units - u0 : kWideMaxUnits;
+    hipLaunchKernelGGL((quest_score_wide_kernel<D, NT, 4>), dim3(256), dim3(kWideWaves * 64), 0, st, a, G, L.hkv, L.ps,
+                       L.hs, L.ts, u0, nu);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 // Scoring path: the matrix-core kernel unless SE_QUEST_SCORE=valu selects

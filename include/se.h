@@ -192,7 +192,7 @@ typedef struct se_snapkv_params {
   int32_t head_dim;        /* D; 128 or 64                                   */
   int32_t max_prompt_len;  /* token dim of k, v: [B, Hkv, max_prompt_len, D] */
   int32_t window;          /* W, 1..64                                        */
-  int32_t pool_kernel;     /* odd, >= 1                                       */
+  int32_t pool_kernel;     /* odd, 1 .. 129 (wider: SE_EUNSUPPORTED)          */
   int32_t budget;          /* R >= 1 prefix tokens kept                       */
   int32_t out_capacity;    /* token dim of k_out/v_out, >= budget + window    */
   float sm_scale;          /* s; 0 means 1/sqrt(D)                            */

@@ -95,6 +95,7 @@ int check_snap(const se_snapkv_params* p) {
   if (p->window < 1 || p->budget < 1) return SE_EINVAL;
   if (p->window > 64) return SE_EUNSUPPORTED;
   if (p->pool_kernel < 1 || p->pool_kernel % 2 == 0) return SE_EINVAL;
+  if (p->pool_kernel > se::kMaxPoolKernel) return SE_EUNSUPPORTED;
   if (p->out_capacity < p->budget + p->window) return SE_EINVAL;
   if (p->max_prompt_len - p->window > 65536) return SE_EUNSUPPORTED;
   if (!(p->sm_scale >= 0.f) || isinf(p->sm_scale)) return SE_EINVAL;

@@ -51,6 +51,8 @@ size_t decode_partials_bytes(const Layout& L, int B, int Hq, int splits);
 hipError_t launch_decode(const Layout& L, const DecodeArgs& a, hipStream_t st);
 
 // ---- SnapKV ----------------------------------------------------------------
+constexpr int kMaxPoolKernel = 129;  // widest max-pool window the pooling kernel stages
+
 struct SnapArgs {
   const uint16_t* q_win;  // [B, Hq, W, D]
   const uint16_t* k;      // [B, Hkv, N, D]

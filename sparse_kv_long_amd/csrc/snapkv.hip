@@ -216,10 +216,12 @@ __global__ __launch_bounds__(128) void snap_rowmerge_kernel(SnapArgs a, const fl
     const float* src = row_part + ((((int64_t)b * a.Hkv + g) * nrg + rg) * slots) * kRowsPerGroup * 2;
     float M = -__builtin_inff();
     for (int s = 0; s < slots; ++s) M = fmaxf(M, src[((int64_t)s * kRowsPerGroup + rr) * 2]);
+    // loads unconditional (a load under a branch waits before the next one issues)
     float S = 0.f;
     for (int s = 0; s < slots; ++s) {
       const float ms = src[((int64_t)s * kRowsPerGroup + rr) * 2];
-      if (ms != -__builtin_inff()) S += src[((int64_t)s * kRowsPerGroup + rr) * 2 + 1] * __builtin_amdgcn_exp2f(ms - M);
+      const float ls = src[((int64_t)s * kRowsPerGroup + rr) * 2 + 1];
+      S += ms == -__builtin_inff() ? 0.f : ls * __builtin_amdgcn_exp2f(ms - M);
     }
     const int hh = r / a.W, i = r % a.W;
     row_c[((int64_t)b * a.Hq + g * G + hh) * a.W + i] = M + __builtin_amdgcn_logf(S);
@@ -311,30 +313,47 @@ hipError_t launch_snap_votes(const SnapArgs& a, const SnapWork& w, bool skip_kep
 }
 
 // ---------------------------------------------------------------------------
-// Max-pool of the votes (summed over row groups).  One thread per position.
+// Max-pool of the votes (summed over row groups).  A block of 256 threads
+// pools 256 positions: it sums the row groups of its positions plus a halo of
+// `radius` on each side once into LDS, then every thread takes the max over
+// its window from LDS.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void maxpool_kernel(const float* __restrict__ votes, const int32_t* __restrict__ lens,
-                                                      float* __restrict__ pooled, int B, int Hkv, int N, int W,
-                                                      int R, int radius, int nrg, int skip_kept) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+constexpr int kPoolTile = 256;
+constexpr int kPoolMaxRadius = kMaxPoolKernel / 2;
+
+__global__ __launch_bounds__(kPoolTile) void maxpool_kernel(const float* __restrict__ votes,
+                                                            const int32_t* __restrict__ lens,
+                                                            float* __restrict__ pooled, int B, int Hkv, int N, int W,
+                                                            int R, int radius, int nrg, int skip_kept) {
+  __shared__ float sv[kPoolTile + 2 * kPoolMaxRadius];
+  const int j0 = blockIdx.x * kPoolTile;
   const int g = blockIdx.y, b = blockIdx.z;
   const int L = lens[b] - W;
-  if (j >= L || (skip_kept && L <= R)) return;
-  const int lo = max(0, j - radius), hi = min(L - 1, j + radius);
-  float best = -__builtin_inff();
-  for (int t = lo; t <= hi; ++t) {
-    float s = 0.f;
-    for (int rg = 0; rg < nrg; ++rg) s += votes[(((int64_t)rg * B + b) * Hkv + g) * N + t];
-    best = fmaxf(best, s);
+  if (j0 >= L || (skip_kept && L <= R)) return;
+  const int span = min(kPoolTile + 2 * radius, L - (j0 - radius));
+  for (int i = threadIdx.x; i < kPoolTile + 2 * radius; i += kPoolTile) {
+    const int t = j0 - radius + i;
+    float v = -__builtin_inff();
+    if (t >= 0 && t < L && i < span) {
+      v = 0.f;
+      for (int rg = 0; rg < nrg; ++rg) v += votes[(((int64_t)rg * B + b) * Hkv + g) * N + t];
+    }
+    sv[i] = v;
   }
+  __syncthreads();
+  const int j = j0 + threadIdx.x;
+  if (j >= L) return;
+  float best = -__builtin_inff();
+  for (int d = 0; d <= 2 * radius; ++d) best = fmaxf(best, sv[threadIdx.x + d]);
   pooled[((int64_t)b * Hkv + g) * N + j] = best;
 }
 
 hipError_t launch_maxpool(const SnapArgs& a, const float* votes, int row_groups, float* pooled, bool skip_kept,
                           hipStream_t st) {
   if (a.B == 0) return hipSuccess;
-  dim3 grid((a.N + 255) / 256, a.Hkv, a.B);
-  hipLaunchKernelGGL(maxpool_kernel, grid, dim3(256), 0, st, votes, a.lens, pooled, a.B, a.Hkv, a.N, a.W, a.R,
+  if (a.pool / 2 > kPoolMaxRadius) return hipErrorInvalidValue;
+  dim3 grid((a.N + kPoolTile - 1) / kPoolTile, a.Hkv, a.B);
+  hipLaunchKernelGGL(maxpool_kernel, grid, dim3(kPoolTile), 0, st, votes, a.lens, pooled, a.B, a.Hkv, a.N, a.W, a.R,
                      a.pool / 2, row_groups, skip_kept ? 1 : 0);
   return hipGetLastError();
 }

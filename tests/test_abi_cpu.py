@@ -114,6 +114,7 @@ def test_decode_misaligned_and_workspace():
 @pytest.mark.parametrize("mutate,code", [
     (lambda p: setattr(p, "pool_kernel", 6), se.SE_EINVAL),
     (lambda p: setattr(p, "pool_kernel", 0), se.SE_EINVAL),
+    (lambda p: setattr(p, "pool_kernel", 131), se.SE_EUNSUPPORTED),
     (lambda p: setattr(p, "window", 0), se.SE_EINVAL),
     (lambda p: setattr(p, "window", 65), se.SE_EUNSUPPORTED),
     (lambda p: setattr(p, "budget", 0), se.SE_EINVAL),

@@ -425,8 +425,8 @@ def cpu_baseline(wl, x, qs, seconds):
     attention -- given the page summaries, which the oracle builds beforehand,
     untimed -- including the decoding of the bf16 inputs it reads) on (request, KV head) units in a seeded order,
     single-threaded, until about `seconds` of CPU time are spent (passing on
-    to the next step's query once every unit of a step is done), and scale
-    to the whole step."""
+    to the next query once every unit of a step is done, cycling through the
+    queries), and scale to the whole step."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -441,9 +441,9 @@ def cpu_baseline(wl, x, qs, seconds):
     spent = 0.0
     done = 0
     summaries = {}
-    while spent < seconds and done < len(units) * len(qs):
+    while spent < seconds and done < 100000:
         b, g = units[int(order[done % len(units)])]
-        qh = bf16_bits(qs[done // len(units)][b])
+        qh = bf16_bits(qs[(done // len(units)) % len(qs)][b])
         n = int(lens[b])
         P = -(-n // 16)
         rows = torch_index(x["k_pages"], pt[b, :P], g)

@@ -26,6 +26,13 @@
 
 namespace se {
 
+// Online softmax with a lazily moved reference max (log2 units): the matrix-
+// core decodes rescale their accumulators only when a head's running max
+// grows by more than this, so every weight stays below 2^kLazyRescale (no
+// overflow in fp32, and the bf16 hi + lo split keeps its relative accuracy)
+// and the rescale, which touches every accumulator, runs on few pages.
+constexpr float kLazyRescale = 8.f;
+
 template <int G, int DK, int DV>
 struct DecodeShape {
   static constexpr int HWMAX = DK <= 128 ? 8 : 4;
@@ -430,17 +437,15 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
       z[i] = (col < G && 4 * kq + i < valid) ? s[i] * scale2 : -__builtin_inff();
       pm = fmaxf(pm, z[i]);
     }
-    pm = fmaxf(pm, __shfl_xor(pm, 16));
-    pm = fmaxf(pm, __shfl_xor(pm, 32));
-    const float m_new = fmaxf(m_run, pm);
-    const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
-    l_run = l_run * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-    m_run = m_new;
-    // rescale the accumulators when some head's max moved (rows are heads 4kq + i)
-    if (__any(alpha != 1.f)) {
+    pm = rows_max(pm);
+    // lazy rescaling: a head's reference max moves only when the page max
+    // passes it by more than kLazyRescale, so most pages skip the rescale
+    const bool grow = pm > m_run + kLazyRescale;
+    if (__any(grow)) {
+      const float alpha = !grow ? 1.f : m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - pm);
+      l_run *= alpha;
+      m_run = grow ? pm : m_run;
+      // rescale the accumulators (rows are heads 4kq + i)
       if (kq == 0) alpha_lds[w][col] = alpha;
       __builtin_amdgcn_wave_barrier();
       const float4 al = *reinterpret_cast<const float4*>(&alpha_lds[w][4 * kq]);
@@ -453,6 +458,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
       }
       __builtin_amdgcn_wave_barrier();
     }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m_run);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
     // weights as hi + lo bf16 pairs, elements e = tokens 4kq + e
     uint32_t hi[2], lo[2];
 #pragma unroll
@@ -557,8 +566,8 @@ template <int NHT, int RD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts, int pps, float scale2) {
   constexpr int DK = 576, DV = 512, NW = 4, PPS = kMlaPagesPerSplit;
-  __shared__ uint4 stage[NW][kPage * 16];     // per wave: 16 tokens x 16 chunks of 8 channels, swizzled
-  __shared__ f32x4_t sbuf[2][NW][NHT][kWave];  // partial logits, double-buffered over pages
+  __shared__ uint4 stage[NW][2][kPage * 16];      // per wave and page of the pair: 16 tokens x 16 chunks, swizzled
+  __shared__ f32x4_t sbuf[2][NW][2 * NHT][kWave];  // partial logits (head tile, page), double-buffered over pairs
   __shared__ float alpha_lds[NW][NHT * 16];
   __shared__ int64_t pid_lds[PPS];
   __shared__ int vld_lds[PPS];
@@ -586,13 +595,6 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
     }
     return;
   }
-  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
-    const int lp = list ? list[p_begin + i] : p_begin + i;
-    pid_lds[i] = plist ? plist[p_begin + i] : a.page_table[(int64_t)b * a.MP + lp];
-    vld_lds[i] = min(kPage, n - lp * kPage);
-  }
-  __syncthreads();
-
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
   const uint16_t* kb = a.k + (int64_t)g * hs;
@@ -600,6 +602,7 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
   const uint16_t* rrow = kb + col * ts + 512 + 16 * w + 4 * kq;   // rope: token col, 4 channels
 
   // q fragments: head 16ht + col; latent channels 128w + 32ks + 8kq, rope 512 + 16w + 4kq
+  // (requested first: their latency overlaps the page-id staging below)
   uint4 qf[NHT][4];
   uint2 qr[NHT];
 #pragma unroll
@@ -610,6 +613,12 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
     for (int ks = 0; ks < 4; ++ks) qf[ht][ks] = ld16(qh + 128 * w + 32 * ks + 8 * kq);
     qr[ht] = *reinterpret_cast<const uint2*>(qh + 512 + 16 * w + 4 * kq);
   }
+  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
+    const int lp = list ? list[p_begin + i] : p_begin + i;
+    pid_lds[i] = plist ? plist[p_begin + i] : a.page_table[(int64_t)b * a.MP + lp];
+    vld_lds[i] = min(kPage, n - lp * kPage);
+  }
+  __syncthreads();
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {
     if (16 * ht + col >= G) {
@@ -639,21 +648,22 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[ht][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  uint4* st = stage[w];
-
-  auto page = [&](int ii, PageRegs& R) {
-    const int valid = vld_lds[ii];
-    const int buf = ii & 1;
-    // restage the wave's 16 x 128 slice as q.k A fragments (token col, channels 8kq + 32ks)
+  // Pages are consumed in pairs: the softmax chain (row max, exponentials,
+  // weight split) is a run of dependent steps whose latency, with one wave
+  // per SIMD, nothing else hides; over two pages at once every step has twice
+  // the independent work, and the block barrier is paid once per pair.
+  auto restage = [&](const PageRegs& R, uint4* st) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 4 * kq + e;
       st[t * 16 + (col ^ (t & 7))] = R.v[e];
     }
-    __builtin_amdgcn_wave_barrier();  // lanes read what other lanes wrote
-    f32x4_t s[NHT];
+  };
+  // this wave's share of the logits: rope (k = 8kq + j, channels 512 + 16w +
+  // 4kq + j for j < 4, zero above), then the latent slice restaged in st
+  auto qk = [&](const PageRegs& R, const uint4* st, f32x4_t (&s)[NHT]) {
 #pragma unroll
-    for (int ht = 0; ht < NHT; ++ht)  // rope: k = 8kq + j, channels 512 + 16w + 4kq + j for j < 4, zero above
+    for (int ht = 0; ht < NHT; ++ht)
       s[ht] = mfma16(make_uint4(R.r.x, R.r.y, 0u, 0u), make_uint4(qr[ht].x, qr[ht].y, 0u, 0u),
                      f32x4_t{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -662,61 +672,99 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
 #pragma unroll
       for (int ht = 0; ht < NHT; ++ht) s[ht] = mfma16(A, qf[ht][ks], s[ht]);
     }
-    __builtin_amdgcn_wave_barrier();  // the next page's restaging waits for these reads
-    // sum the four waves' channel shares (scaled to the log2 domain) in a fixed order
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      f32x4_t u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = s[ht][i] * scale2;
-      sbuf[buf][w][ht][lane] = u;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ht = 0; ht < NHT; ++ht) {
-      f32x4_t t = sbuf[buf][0][ht][lane];
-#pragma unroll
-      for (int q = 1; q < NW; ++q) {
-        const f32x4_t u = sbuf[buf][q][ht][lane];
-        t[0] += u[0];
-        t[1] += u[1];
-        t[2] += u[2];
-        t[3] += u[3];
-      }
-      s[ht] = t;
-    }
+  };
+  // value fragments: {channel 8col + nt of tokens 4kq + 0, 1} and {.. 2, 3};
+  // rows past the sequence are zeroed (those slots may hold anything)
+  auto vfrag = [&](PageRegs& R, int valid, uint32_t (&vfr)[8][2]) {
     if (valid < kPage) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (4 * kq + e >= valid) R.v[e] = make_uint4(0, 0, 0, 0);  // slots past the sequence may hold anything
+        if (4 * kq + e >= valid) R.v[e] = make_uint4(0, 0, 0, 0);
     }
-    uint32_t vfr[8][2];
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
       const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
       vfr[nt][0] = __builtin_amdgcn_perm(dword(R.v[1], nt >> 1), dword(R.v[0], nt >> 1), sel);
       vfr[nt][1] = __builtin_amdgcn_perm(dword(R.v[3], nt >> 1), dword(R.v[2], nt >> 1), sel);
     }
+  };
+  // weights as hi + lo bf16 pairs along k: k = 8kq + j, hi (j < 4) and lo (j >= 4) of tokens 4kq + j
+  auto split_hi_lo = [](const float* p) -> uint4 {
+    uint32_t hi[2], lo[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      const uint32_t h0 = __float_as_uint(p[2 * d]) & 0xffff0000u, h1 = __float_as_uint(p[2 * d + 1]) & 0xffff0000u;
+      const uint32_t l0 = __float_as_uint(p[2 * d] - __uint_as_float(h0));
+      const uint32_t l1 = __float_as_uint(p[2 * d + 1] - __uint_as_float(h1));
+      hi[d] = (h0 >> 16) | h1;
+      lo[d] = (l0 >> 16) | (l1 & 0xffff0000u);
+    }
+    return make_uint4(hi[0], hi[1], lo[0], lo[1]);
+  };
+
+  // pages ii and ii + 1 (the second absent, and all its weights zero, when ii + 1 == npg)
+  auto pair = [&](int ii, PageRegs& RA, PageRegs& RB) {
+    const int vA = vld_lds[ii];
+    const int vB = ii + 1 < npg ? vld_lds[ii + 1] : 0;
+    const int buf = (ii >> 1) & 1;
+    restage(RA, stage[w][0]);
+    restage(RB, stage[w][1]);
+    __builtin_amdgcn_wave_barrier();  // lanes read what other lanes wrote
+    f32x4_t sA[NHT], sB[NHT];
+    qk(RA, stage[w][0], sA);
+    qk(RB, stage[w][1], sB);
+    __builtin_amdgcn_wave_barrier();  // the next pair's restaging waits for these reads
+    // sum the four waves' channel shares (scaled to the log2 domain) in a fixed order
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      f32x4_t u, v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u[i] = sA[ht][i] * scale2;
+        v[i] = sB[ht][i] * scale2;
+      }
+      sbuf[buf][w][2 * ht][lane] = u;
+      sbuf[buf][w][2 * ht + 1][lane] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ht = 0; ht < NHT; ++ht) {
+      f32x4_t t = sbuf[buf][0][2 * ht][lane], t2 = sbuf[buf][0][2 * ht + 1][lane];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) {
+        const f32x4_t u = sbuf[buf][q][2 * ht][lane], v = sbuf[buf][q][2 * ht + 1][lane];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          t[i] += u[i];
+          t2[i] += v[i];
+        }
+      }
+      sA[ht] = t;
+      sB[ht] = t2;
+    }
+    uint32_t vfA[8][2], vfB[8][2];
+    vfrag(RA, vA, vfA);
+    vfrag(RB, vB, vfB);
 #pragma unroll
     for (int ht = 0; ht < NHT; ++ht) {
       const bool hv = 16 * ht + col < G;
-      float z[4];
+      float z[8];
       float pm = -__builtin_inff();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        z[i] = (hv && 4 * kq + i < valid) ? s[ht][i] : -__builtin_inff();
-        pm = fmaxf(pm, z[i]);
+        z[i] = (hv && 4 * kq + i < vA) ? sA[ht][i] : -__builtin_inff();
+        z[4 + i] = (hv && 4 * kq + i < vB) ? sB[ht][i] : -__builtin_inff();
       }
-      pm = fmaxf(pm, __shfl_xor(pm, 16));
-      pm = fmaxf(pm, __shfl_xor(pm, 32));
-      const float m_new = fmaxf(m_run[ht], pm);
-      const float alpha = m_new == -__builtin_inff() ? 1.f : __builtin_amdgcn_exp2f(m_run[ht] - m_new);
-      float p[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m_new);
-      l_run[ht] = l_run[ht] * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-      m_run[ht] = m_new;
-      if (__any(alpha != 1.f)) {
+      for (int i = 0; i < 8; ++i) pm = fmaxf(pm, z[i]);
+      pm = rows_max(pm);
+      // lazy rescaling, as in the GQA kernel
+      const bool grow = pm > m_run[ht] + kLazyRescale;
+      if (__any(grow)) {
+        const float alpha =
+            !grow ? 1.f : m_run[ht] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run[ht] - pm);
+        l_run[ht] *= alpha;
+        m_run[ht] = grow ? pm : m_run[ht];
         if (kq == 0) alpha_lds[w][16 * ht + col] = alpha;
         __builtin_amdgcn_wave_barrier();
         const float4 al = *reinterpret_cast<const float4*>(&alpha_lds[w][16 * ht + 4 * kq]);
@@ -729,34 +777,37 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
         }
         __builtin_amdgcn_wave_barrier();
       }
-      uint32_t hi[2], lo[2];
+      float p[8];
 #pragma unroll
-      for (int d = 0; d < 2; ++d) {
-        const uint32_t h0 = __float_as_uint(p[2 * d]) & 0xffff0000u, h1 = __float_as_uint(p[2 * d + 1]) & 0xffff0000u;
-        const uint32_t l0 = __float_as_uint(p[2 * d] - __uint_as_float(h0));
-        const uint32_t l1 = __float_as_uint(p[2 * d + 1] - __uint_as_float(h1));
-        hi[d] = (h0 >> 16) | h1;
-        lo[d] = (l0 >> 16) | (l1 & 0xffff0000u);
+      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(z[i] - m_run[ht]);
+      l_run[ht] += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      const uint4 paA = split_hi_lo(p), paB = split_hi_lo(p + 4);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        acc[ht][nt] = mfma16(paA, make_uint4(vfA[nt][0], vfA[nt][1], vfA[nt][0], vfA[nt][1]), acc[ht][nt]);
+        acc[ht][nt] = mfma16(paB, make_uint4(vfB[nt][0], vfB[nt][1], vfB[nt][0], vfB[nt][1]), acc[ht][nt]);
       }
-      const uint4 pa = make_uint4(hi[0], hi[1], lo[0], lo[1]);  // k = 8kq + j: hi (j < 4), lo (j >= 4)
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt)
-        acc[ht][nt] = mfma16(pa, make_uint4(vfr[nt][0], vfr[nt][1], vfr[nt][0], vfr[nt][1]), acc[ht][nt]);
     }
   };
 
   {
-    // RD pages in the register ring (RD - 1 in flight while one is consumed):
-    // the block is alone on its CU, so deep prefetch is what keeps HBM busy
+    // RD pages in the register ring, consumed two at a time (RD - 2 in
+    // flight while a pair is processed): the block is alone on its CU, so
+    // deep prefetch is what keeps HBM busy
+    static_assert(RD % 2 == 0 && RD >= 4, "the ring holds whole pairs");
     PageRegs r[RD];
 #pragma unroll
-    for (int j = 0; j < RD - 1; ++j) load(j, r[j]);
+    for (int j = 0; j < RD - 2; ++j) {
+      load(j, r[j]);
+      __builtin_amdgcn_sched_barrier(0);  // issue order = use order, so each wait covers one page
+    }
     for (int ii = 0; ii < npg; ii += RD) {
 #pragma unroll
-      for (int j = 0; j < RD; ++j) {
+      for (int j = 0; j < RD; j += 2) {
+        load(ii + j + RD - 2, r[(j + RD - 2) % RD]);
         load(ii + j + RD - 1, r[(j + RD - 1) % RD]);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetches ahead of the compute
-        if (j == 0 || ii + j < npg) page(ii + j, r[j]);
+        if (j == 0 || ii + j < npg) pair(ii + j, r[j], r[j + 1]);
       }
     }
   }
@@ -790,12 +841,60 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
 // loads unconditional, so they are issued back to back.
 constexpr int kMaxSplits = 1024;
 
+// Few splits (the common case): every thread loads all (m, l) pairs of its
+// (request, head) and four acc columns of every split at once, so the merge
+// takes one memory round trip and no barrier.  Indices past nsplit are
+// clamped and masked.
+constexpr int kMergeFew = 16;
+
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_acc,
                                                     const float* __restrict__ part_ml, float* __restrict__ out,
                                                     int nsplit, int DV) {
   __shared__ float wts[kMaxSplits];
   const int64_t bh = blockIdx.x;
   const float* ml = part_ml + bh * nsplit * 2;
+  const float* acc = part_acc + bh * nsplit * DV;
+  if (nsplit <= kMergeFew) {
+    for (int c = 4 * threadIdx.x; c < DV; c += 4 * blockDim.x) {
+      float m[kMergeFew], l[kMergeFew];
+      float4 v[kMergeFew];
+#pragma unroll
+      for (int sp = 0; sp < kMergeFew; ++sp) {
+        const int s = min(sp, nsplit - 1);
+        m[sp] = ml[2 * s];
+        l[sp] = ml[2 * s + 1];
+        v[sp] = *reinterpret_cast<const float4*>(acc + (int64_t)s * DV + c);
+      }
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int sp = 0; sp < kMergeFew; ++sp) M = fmaxf(M, m[sp]);
+      float den = 0.f;
+      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int sp = 0; sp < kMergeFew; ++sp) {
+        // an empty split (m = -inf) never wrote its acc; a clamped duplicate
+        // (sp >= nsplit) is not counted
+        const bool live = sp < nsplit && m[sp] != -__builtin_inff();
+        const float wgt = live ? __builtin_amdgcn_exp2f(m[sp] - M) : 0.f;
+        den += wgt * l[sp];
+        num.x += live ? wgt * v[sp].x : 0.f;
+        num.y += live ? wgt * v[sp].y : 0.f;
+        num.z += live ? wgt * v[sp].z : 0.f;
+        num.w += live ? wgt * v[sp].w : 0.f;
+      }
+      const float inv = den > 0.f ? 1.f / den : 0.f;
+      float* o = out + bh * DV + c;
+      if ((reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+        *reinterpret_cast<float4*>(o) = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+      } else {  // the output need only be 4-byte aligned
+        o[0] = num.x * inv;
+        o[1] = num.y * inv;
+        o[2] = num.z * inv;
+        o[3] = num.w * inv;
+      }
+    }
+    return;
+  }
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     float M = -__builtin_inff();
@@ -816,7 +915,6 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   __syncthreads();
   // an empty split never wrote its acc: its weight is 0 and its acc is not used
   auto term = [&](int sp, float a) { return wts[sp] != 0.f ? wts[sp] * a : 0.f; };
-  const float* acc = part_acc + bh * nsplit * DV;
   for (int c = threadIdx.x; c < DV; c += blockDim.x) {
     float num = 0.f;
     int sp = 0;
@@ -910,7 +1008,8 @@ template <int NHT>
 static hipError_t launch_mla(const Layout& L, const DecodeArgs& a, int pps, hipStream_t st) {
   const float scale2 = a.scale * kLog2e;
   dim3 grid(a.splits, L.hkv, a.B);
-  hipLaunchKernelGGL((decode_mla_kernel<NHT, 3>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, pps, scale2);
+  // six pages in the register ring: two pairs in flight while one is processed
+  hipLaunchKernelGGL((decode_mla_kernel<NHT, 6>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, pps, scale2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, st, a.part_acc, a.part_ml, a.out, a.splits, 512);

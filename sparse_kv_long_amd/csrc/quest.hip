@@ -138,226 +138,6 @@ __device__ __forceinline__ void minmax8(const uint16_t* src, int64_t ts, int val
 }
 
 // ---------------------------------------------------------------------------
-// K1, register kernel: G * D <= 1024 (q+ and q- of the lane's channels of all
-// G heads stay in registers).  Grid (ceil(MP / (4*ppw)), Hkv, B), 4 waves per
-// block, each wave scores `ppw` consecutive pages of one (request, KV head).
-// With `refresh`, the wave holding the request's last page first rebuilds
-// that page's summary from its keys, stores it, and scores it from the
-// rebuilt values.
-// ---------------------------------------------------------------------------
-template <int G, int D, bool SUM>
-__global__ __launch_bounds__(256) void quest_score_reg_kernel(ScoreArgs a, int Hkv, int64_t ps, int64_t hs,
-                                                               int64_t ts, int ppw) {
-  constexpr int LPP = 8;
-  constexpr int NCH = D / 4;      // 16-byte chunks per record
-  constexpr int CPL = NCH / LPP;  // chunks per lane
-  constexpr int NCC = CPL / 2;    // channel chunks per lane
-  constexpr int U = 2;            // pages per lane group per stage (a stage is 8*U pages)
-  static_assert((D / 8) % LPP == 0, "channel chunks must split evenly over the 8 lanes of a record");
-  __shared__ int32_t ids[4 * kMaxPagesPerWave];
-
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int j = lane & 7, pg = lane >> 3;
-  const int n = a.seq_lens[b];
-  const int P = (n + kPage - 1) / kPage;
-  const bool dense = a.topk >= P;
-  const int blk_start = blockIdx.x * 4 * ppw;
-  if (blk_start >= P) return;
-  const int blk_end = min(blk_start + 4 * ppw, P);
-  const int plast = P - 1;
-  const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
-  // stage the block's physical page ids in LDS (one coalesced pass)
-  if (!dense)
-    for (int i = threadIdx.x; i < blk_end - blk_start; i += blockDim.x) ids[i] = ptrow[blk_start + i];
-  __syncthreads();
-
-  const int start = blk_start + wave * ppw;
-  int end = min(start + ppw, P);
-  if (start >= end) return;
-  const bool do_refresh = a.refresh && plast >= start && plast < end;
-  if (dense && !do_refresh) return;
-  if (a.refresh) end = min(end, plast);
-
-  uint4 qn[G][NCC], qp[G][NCC];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + g * G + h) * D;
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) qn[h][cc] = split_neg(ld16(qrow + 8 * (j + LPP * cc)), qp[h][cc]);
-  }
-
-  const int64_t rec_stride = 2 * D;
-  const uint16_t* summ_g = a.summ + (int64_t)g * rec_stride + 8 * j;
-  const int64_t pid_stride = (int64_t)Hkv * rec_stride;
-  float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
-
-  auto page_score = [&](const uint4 (&d)[CPL]) -> float {
-    float acc[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) acc[h] = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        acc[h] = dot8(qn[h][cc], d[cc], acc[h]);
-        acc[h] = dot8(qp[h][cc], d[NCC + cc], acc[h]);
-      }
-    }
-    float r = 0.f;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float v = group_sum<LPP>(acc[h]);
-      r = (h == 0) ? v : (SUM ? r + v : fmaxf(r, v));
-    }
-    return r * a.scale;
-  };
-
-  if (!dense && start < end) {
-    // Two register stages of 8*U pages: the next stage's loads are in flight
-    // while the current one is scored.  Loads are unconditional (page index
-    // clamped to the range; a clamped stage re-reads cached records) so that
-    // no branch sits between a load and its use; only the stores are masked.
-    const int nst = (end - start + 8 * U - 1) / (8 * U);
-    uint4 dA[U][CPL], dB[U][CPL];
-    auto load = [&](int st, uint4 (&d)[U][CPL]) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int p = min(start + st * 8 * U + 8 * u + pg, end - 1);
-        const uint16_t* rec = summ_g + (int64_t)ids[p - blk_start] * pid_stride;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) d[u][c] = ldnt16(rec + 8 * LPP * c);
-      }
-    };
-    auto score = [&](int st, const uint4 (&d)[U][CPL]) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int p = start + st * 8 * U + 8 * u + pg;
-        const float sc = page_score(d[u]);
-        if (p < end && j == 0) srow[p] = sc;
-      }
-    };
-    load(0, dA);
-    for (int st = 0; st < nst; st += 2) {
-      load(min(st + 1, nst - 1), dB);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-      score(st, dA);
-      load(min(st + 2, nst - 1), dA);
-      __builtin_amdgcn_sched_barrier(0);
-      score(st + 1, dB);
-    }
-  }
-
-  if (do_refresh) {
-    const int64_t pid = ptrow[plast];
-    const int valid = n - plast * kPage;
-    const uint16_t* kb = a.k + pid * ps + (int64_t)g * hs;
-    uint4 d[CPL];
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) minmax8(kb + 8 * (j + LPP * cc), ts, valid, d[cc], d[NCC + cc]);
-    uint16_t* rec = a.summ + (pid * Hkv + g) * rec_stride + 8 * j;
-    if (pg == 0) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) *reinterpret_cast<uint4*>(rec + 8 * LPP * c) = d[c];
-    }
-    const float sc = page_score(d);
-    if (!dense && lane == 0) srow[plast] = sc;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// K1, generic kernel: any G <= 64 and D in {64, 128, 576}.  q+ and q- of all
-// heads live in LDS; each lane keeps its chunks of the record in registers
-// and loops over the heads.  Same grid and refresh rule as above.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void quest_score_lds_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs,
-                                                              int64_t ts, int ppw) {
-  constexpr int LPP = 8;
-  constexpr int NCH = D / 4;
-  constexpr int CPL = NCH / LPP;
-  constexpr int NCC = CPL / 2;
-  constexpr int DC = D / 8;  // channel chunks per head
-  static_assert(DC % LPP == 0, "channel chunks must split evenly over the 8 lanes of a record");
-  extern __shared__ uint4 qs[];  // [G][DC] q-  then [G][DC] q+
-
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j = lane & 7, pg = lane >> 3;
-  const int n = a.seq_lens[b];
-  const int P = (n + kPage - 1) / kPage;
-  const bool dense = a.topk >= P;
-  uint4* qneg = qs;
-  uint4* qpos = qs + G * DC;
-  for (int i = threadIdx.x; i < G * DC; i += blockDim.x) {
-    const int h = i / DC, c = i % DC;
-    uint4 pos;
-    qneg[i] = split_neg(ld16(a.q + ((int64_t)b * a.Hq + g * G + h) * D + 8 * c), pos);
-    qpos[i] = pos;
-  }
-  __syncthreads();
-
-  const int start = (blockIdx.x * 4 + wave) * ppw;
-  int end = min(start + ppw, P);
-  if (start >= end) return;
-  const int plast = P - 1;
-  const bool do_refresh = a.refresh && plast >= start && plast < end;
-  if (dense && !do_refresh) return;
-  if (a.refresh) end = min(end, plast);
-
-  const int64_t rec_stride = 2 * D;
-  const uint16_t* summ_g = a.summ + (int64_t)g * rec_stride;
-  float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
-  const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
-  const bool SUM = a.head_sum != 0;
-
-  auto page_score = [&](const uint4 (&d)[CPL]) -> float {
-    float r = 0.f;
-    for (int h = 0; h < G; ++h) {
-      float acc = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < NCC; ++cc) {
-        acc = dot8(qneg[h * DC + j + LPP * cc], d[cc], acc);
-        acc = dot8(qpos[h * DC + j + LPP * cc], d[NCC + cc], acc);
-      }
-      const float v = group_sum<LPP>(acc);
-      r = (h == 0) ? v : (SUM ? r + v : fmaxf(r, v));
-    }
-    return r * a.scale;
-  };
-
-  if (!dense) {
-    for (int p0 = start; p0 < end; p0 += 8) {
-      const int p = p0 + pg;
-      const bool ok = p < end;
-      const int64_t pid = ok ? ptrow[p] : 0;
-      uint4 d[CPL];
-      const uint16_t* rec = summ_g + pid * Hkv * rec_stride + 8 * j;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) d[c] = ok ? ld16(rec + 8 * LPP * c) : make_uint4(0, 0, 0, 0);
-      const float sc = page_score(d);
-      if (ok && j == 0) srow[p] = sc;
-    }
-  }
-
-  if (do_refresh) {
-    const int64_t pid = ptrow[plast];
-    const int valid = n - plast * kPage;
-    const uint16_t* kb = a.k + pid * ps + (int64_t)g * hs;
-    uint4 d[CPL];
-#pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) minmax8(kb + 8 * (j + LPP * cc), ts, valid, d[cc], d[NCC + cc]);
-    uint16_t* rec = a.summ + (pid * Hkv + g) * rec_stride + 8 * j;
-    if (pg == 0) {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) *reinterpret_cast<uint4*>(rec + 8 * LPP * c) = d[c];
-    }
-    const float sc = page_score(d);
-    if (!dense && lane == 0) srow[plast] = sc;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // K1, matrix-core kernel.  The page bound is a dense contraction,
 //   score[page][h] = sum_k rec[page][k] * qq[h][k],  k < 2D,
 // with rec = [min | max] (the stored summary record) and qq = [q- | q+], so
@@ -452,6 +232,37 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
     }
   };
 
+  // the refreshed last page first: its dependent chain (keys, min/max, store,
+  // score) then overlaps the streaming of this wave's other pages instead of
+  // trailing it
+  if (do_refresh) {
+    const int64_t pid = ptrow[plast];
+    const int valid = n - plast * kPage;
+    const int dc = D / 8;
+    uint16_t* rec = a.summ + (pid * Hkv + g) * 2 * D;
+    for (int ci = lane; ci < NCH; ci += 64) {
+      uint4 mn, mx;
+      minmax8(a.k + pid * ps + (int64_t)g * hs + 8 * (ci < dc ? ci : ci - dc), ts, valid, mn, mx);
+      const uint4 v = ci < dc ? mn : mx;
+      *reinterpret_cast<uint4*>(rec + 8 * ci) = v;
+      refresh_rec[wave][ci] = v;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (!dense) {
+      f32x4_t acc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 d = col == 0 ? refresh_rec[wave][kq + 4 * ks] : make_uint4(0, 0, 0, 0);
+          acc[nt] = mfma16(d, bfrag(nt, ks), acc[nt]);
+        }
+      }
+      finish(acc, plast, plast + 1);  // page slot 0 of the tile is the last page
+    }
+  }
+
   if (!dense && start < end) {
     const int ntile = (end - start + 15) / 16;
     // Records are fetched 8 lanes per record (one full 128-byte line per
@@ -503,33 +314,6 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
     }
   }
 
-  if (do_refresh) {
-    const int64_t pid = ptrow[plast];
-    const int valid = n - plast * kPage;
-    const int dc = D / 8;
-    uint16_t* rec = a.summ + (pid * Hkv + g) * 2 * D;
-    for (int ci = lane; ci < NCH; ci += 64) {
-      uint4 mn, mx;
-      minmax8(a.k + pid * ps + (int64_t)g * hs + 8 * (ci < dc ? ci : ci - dc), ts, valid, mn, mx);
-      const uint4 v = ci < dc ? mn : mx;
-      *reinterpret_cast<uint4*>(rec + 8 * ci) = v;
-      refresh_rec[wave][ci] = v;
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (!dense) {
-      f32x4_t acc[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const uint4 d = col == 0 ? refresh_rec[wave][kq + 4 * ks] : make_uint4(0, 0, 0, 0);
-          acc[nt] = mfma16(d, bfrag(nt, ks), acc[nt]);
-        }
-      }
-      finish(acc, plast, plast + 1);  // page slot 0 of the tile is the last page
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -696,17 +480,23 @@ void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs
       // RD tiles in the register ring: RD - 1 in flight while one is staged and scored
       uint4 r[RD][CPT];
 #pragma unroll
-      for (int j = 0; j < RD - 1; ++j) load(min(j, ntile - 1), r[j]);
+      for (int j = 0; j < RD - 1; ++j) {
+        load(min(j, ntile - 1), r[j]);
+        __builtin_amdgcn_sched_barrier(0);  // issue order = use order
+      }
+      // The prefetch is issued on every step, also past the last tile (a
+      // clamped repeat of it, served by the caches): with a fixed number of
+      // loads between a tile's issue and its use, the compiler waits for that
+      // tile alone instead of draining the whole ring.
       for (int t = 0; t < ntile; t += RD) {
 #pragma unroll
         for (int j = 0; j < RD; ++j) {
-          if (j == 0 || t + j < ntile) {
-            stage(r[j]);
-            __syncthreads();
-            load(min(t + j + RD - 1, ntile - 1), r[(j + RD - 1) % RD]);
-            __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-            score(t + j);
-          }
+          const bool live = j == 0 || t + j < ntile;
+          if (live) stage(r[j]);
+          __syncthreads();
+          load(min(t + j + RD - 1, ntile - 1), r[(j + RD - 1) % RD]);
+          __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
+          if (live) score(t + j);
         }
       }
     }
@@ -764,31 +554,6 @@ static int pick_ppw(int B, int Hkv, int MP) {
   return (int)ppw;
 }
 
-template <int G, int D>
-static hipError_t launch_reg(const Layout& L, const ScoreArgs& a, hipStream_t st) {
-  const int ppw = pick_ppw(a.B, L.hkv, a.MP);
-  dim3 grid((a.MP + 4 * ppw - 1) / (4 * ppw), L.hkv, a.B);
-  if (a.head_sum)
-    hipLaunchKernelGGL((quest_score_reg_kernel<G, D, true>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, ppw);
-  else
-    hipLaunchKernelGGL((quest_score_reg_kernel<G, D, false>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, ppw);
-  return hipGetLastError();
-}
-
-template <int D>
-static hipError_t launch_lds(const Layout& L, const ScoreArgs& a, int G, hipStream_t st) {
-  const int ppw = pick_ppw(a.B, L.hkv, a.MP);
-  dim3 grid((a.MP + 4 * ppw - 1) / (4 * ppw), L.hkv, a.B);
-  const size_t lds = (size_t)2 * G * (D / 8) * sizeof(uint4);
-  if (lds > 65536) {
-    const hipError_t e =
-        hipFuncSetAttribute((const void*)quest_score_lds_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  hipLaunchKernelGGL((quest_score_lds_kernel<D>), grid, dim3(256), lds, st, a, G, L.hkv, L.ps, L.hs, L.ts, ppw);
-  return hipGetLastError();
-}
-
 template <int D, int NT>
 static hipError_t launch_mfma(const Layout& L, const ScoreArgs& a, int G, hipStream_t st) {
   const int ppw = pick_ppw(a.B, L.hkv, a.MP);
@@ -816,33 +581,12 @@ static hipError_t launch_wide(const Layout& L, const ScoreArgs& a, int G, hipStr
   return hipSuccess;
 }
 
-// Scoring path: the matrix-core kernel unless SE_QUEST_SCORE=valu selects
-// the VALU kernels (kept for comparison).
-static bool use_valu_scoring() {
-  static const bool v = [] {
-    const char* e = getenv("SE_QUEST_SCORE");
-    return e && strcmp(e, "valu") == 0;
-  }();
-  return v;
-}
-
 hipError_t launch_quest_scores(const Layout& L, const ScoreArgs& a, hipStream_t st) {
   const int G = a.Hq / L.hkv;
   if (a.B == 0 || a.MP == 0) return hipSuccess;
-  if (!use_valu_scoring()) {
-    if (L.dk == 64) return G <= 16 ? launch_mfma<64, 1>(L, a, G, st) : launch_mfma<64, 2>(L, a, G, st);
-    if (L.dk == 128) return G <= 16 ? launch_mfma<128, 1>(L, a, G, st) : launch_mfma<128, 2>(L, a, G, st);
-    if (L.dk == 576) return G <= 16 ? launch_wide<576, 1>(L, a, G, st) : launch_wide<576, 2>(L, a, G, st);
-    return hipErrorInvalidValue;
-  }
-#define SE_REG(GG, DD) \
-  if (G == GG && L.dk == DD) return launch_reg<GG, DD>(L, a, st);
-  SE_REG(1, 64) SE_REG(2, 64) SE_REG(4, 64) SE_REG(8, 64) SE_REG(16, 64)
-  SE_REG(1, 128) SE_REG(2, 128) SE_REG(4, 128) SE_REG(8, 128)
-#undef SE_REG
-  if (L.dk == 64) return launch_lds<64>(L, a, G, st);
-  if (L.dk == 128) return launch_lds<128>(L, a, G, st);
-  if (L.dk == 576) return launch_lds<576>(L, a, G, st);
+  if (L.dk == 64) return G <= 16 ? launch_mfma<64, 1>(L, a, G, st) : launch_mfma<64, 2>(L, a, G, st);
+  if (L.dk == 128) return G <= 16 ? launch_mfma<128, 1>(L, a, G, st) : launch_mfma<128, 2>(L, a, G, st);
+  if (L.dk == 576) return G <= 16 ? launch_wide<576, 1>(L, a, G, st) : launch_wide<576, 2>(L, a, G, st);
   return hipErrorInvalidValue;
 }
 

@@ -8,8 +8,8 @@
 //
 // Method: scores map to order-preserving 32-bit keys held in registers (each
 // thread owns KPT consecutive indices).  The bits common to every key are
-// found with a block-wide AND/OR; radix passes of up to 8 bits over the rest,
-// each a 256-bin LDS histogram of the keys that still match the chosen
+// found with a block-wide AND/OR; radix passes of up to 11 bits over the rest,
+// each a 2048-bin LDS histogram of the keys that still match the chosen
 // prefix, find the exact k-th largest key T and how many keys equal to T must
 // be taken.
 // Two block-wide exclusive scans then give every thread the number of

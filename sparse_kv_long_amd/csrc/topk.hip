@@ -158,9 +158,12 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ row, int N,
       if (base + i < N && (key[i] & pmask) == prefix) atomicAdd(&H[(key[i] >> lo) & dmask], 1u);
     __syncthreads();
     if (tid < kWave) {
-      // lane t owns bins BPL*t .. BPL*t + BPL-1; only the lane whose range holds
-      // the threshold walks its bins a second time
+      // lane t owns bins BPL*t .. BPL*t + BPL-1; a scan of the lane totals
+      // finds the lane t* whose range holds the threshold, then lanes 0..31
+      // take one bin of that range each (highest first) and a second scan
+      // with a ballot finds the bin: two scans instead of a serial walk
       constexpr int BPL = kRadixBins / kWave;
+      static_assert(BPL <= kWave, "one bin per lane in the second scan");
       const uint4* h4 = reinterpret_cast<const uint4*>(&H[BPL * tid]);
       int local = 0;
 #pragma unroll
@@ -170,19 +173,18 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ row, int N,
       }
       const int incl = wave_incl_scan(local);
       const int total = __builtin_amdgcn_readlane(incl, 63);
-      int above = total - incl;  // keys in bins >= BPL * (tid + 1)
-      if (above < rem && above + local >= rem) {
-        int d = BPL * tid, cnt = 0;
-        for (int j = BPL - 1; j >= 0; --j) {
-          const int cj = (int)H[BPL * tid + j];
-          if (above + cj >= rem) {
-            d = BPL * tid + j;
-            cnt = cj;
-            break;
-          }
-          above += cj;
-        }
-        sm.digit = d;
+      const int above_t = total - incl;  // keys in bins >= BPL * (tid + 1)
+      // exactly one lane holds the threshold: 0 < rem <= total
+      const int ts = __builtin_ctzll(__ballot(above_t < rem && above_t + local >= rem));
+      const int above_s = __builtin_amdgcn_readlane(above_t, ts);
+      const int j = tid < BPL ? tid : 0;
+      const int c = tid < BPL ? (int)H[BPL * ts + (BPL - 1 - j)] : 0;
+      const int cum = wave_incl_scan(c);  // keys in bins BPL*ts + BPL-1-j .. BPL*ts + BPL-1
+      const int js = __builtin_ctzll(__ballot(tid < BPL && above_s + cum >= rem));
+      if (tid == 0) {
+        const int cnt = __builtin_amdgcn_readlane(c, js);
+        const int above = above_s + __builtin_amdgcn_readlane(cum, js) - cnt;
+        sm.digit = BPL * ts + (BPL - 1 - js);
         sm.above = above;
         sm.done = (cnt == rem - above) ? 1 : 0;
       }

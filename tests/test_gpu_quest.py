@@ -176,7 +176,9 @@ def test_split_count_invariance_and_determinism(name):
     summ = build_summaries(x, wl)
     base = summ.clone()
     outs = []
-    for splits in (1, 3, 0, 0):
+    # up to 16 splits the merge takes its one-round-trip path, above it the
+    # LDS path (d128_g8 keeps 20 pages: 20 requested splits give 20)
+    for splits in (1, 3, 16, 20, 0, 0):
         summ.copy_(base)
         o, s = run_sparse_decode(x, wl, summ, splits=splits)
         outs.append((to_np(o), to_np(s)))
@@ -187,7 +189,25 @@ def test_split_count_invariance_and_determinism(name):
     for o, s in outs[1:]:
         assert (s == outs[0][1]).all()
         np.testing.assert_allclose(o, outs[0][0], rtol=0, atol=2.0**-14 * vmax)
-    assert (outs[2][0] == outs[3][0]).all(), "repeated call not bitwise identical"
+    assert (outs[-2][0] == outs[-1][0]).all(), "repeated call not bitwise identical"
+
+
+@pytest.mark.parametrize("name", ["d128_g8", "mla"])
+def test_large_logit_range_matches_oracle(name):
+    """Queries scaled by 16 spread the logits over a range of hundreds, so the
+    decode's running max jumps by more than its lazy-rescale threshold on some
+    pages and by less on others; the result still matches the oracle."""
+    wl, x = make(name)
+    x["q"] = (x["q"].float() * 16).to(torch.bfloat16)
+    summ = build_summaries(x, wl)
+    out, sel = run_sparse_decode(x, wl, summ, refresh=1)
+    h = host_inputs(x)
+    sel_np = to_np(sel)
+    ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], sel_lists(sel_np, h["lens"]), wl.group,
+                                  wl.scale, wl.head_dim_v, wl.v_is_k_prefix)
+    vmax = float(torch.nan_to_num(x["v_pages"] if x["v_pages"] is not None else x["k_pages"], 0.0).abs().max())
+    assert np.isfinite(to_np(out)).all()
+    check_attention(to_np(out), ref, vmax, f"{name} q*16")
 
 
 def test_empty_and_single_token_requests():

@@ -333,17 +333,17 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
 // KW-1), reading their A fragments from LDS without bank conflicts and keeping
 // their q+/q- fragments in registers.  The partial tiles are summed through
 // LDS in a fixed order and waves 0..3 finish rows i = w (pages 4*kq + w of the
-// tile).  Twelve waves of three k-steps each keep the registers per wave small
-// enough for a deep ring, which is what keeps HBM busy with one block per CU.
+// tile).  Four waves of nine k-steps each, one block per CU: measured faster
+// than twelve or six waves of fewer k-steps, and than deeper rings.
 // ---------------------------------------------------------------------------
-constexpr int kWideChunk = 2048;     // page ids staged per pass over a segment
-constexpr int kWideWaves = 12;
-constexpr int kWideMaxUnits = 4096;  // units per launch (prefix sums live in LDS)
+constexpr int kWideChunk = 1024;     // page ids staged per pass over a segment
+constexpr int kWideWaves = 4;
+constexpr int kWideMaxUnits = 2048;  // units per launch (prefix sums live in LDS)
 
-template <int D, int NT, int RD>
-__global__ __launch_bounds__(kWideWaves * 64)
+template <int D, int NT, int RD, int NW>
+__global__ __launch_bounds__(NW * 64)
 void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs, int64_t ts, int u0, int nunits) {
-  constexpr int NW = kWideWaves, NTH = NW * 64;
+  constexpr int NTH = NW * 64;
   constexpr int KS = 2 * D / 32;  // k steps per tile
   constexpr int KW = KS / NW;     // k steps per wave
   constexpr int NCH = D / 4;      // 16-byte chunks per record
@@ -569,12 +569,14 @@ static hipError_t launch_mfma(const Layout& L, const ScoreArgs& a, int G, hipStr
 
 template <int D, int NT>
 static hipError_t launch_wide(const Layout& L, const ScoreArgs& a, int G, hipStream_t st) {
-  // one block per CU (its LDS allows no more); units in launches of at most kWideMaxUnits
+  // one block of four waves per CU, a three-tile ring (measured on the MLA
+  // workload: 46 us, against 48 us for twelve or six waves and 52-54 us for
+  // deeper rings); units in launches of at most kWideMaxUnits
   const int units = a.B * L.hkv;
   for (int u0 = 0; u0 < units; u0 += kWideMaxUnits) {
     const int nu = units - u0 < kWideMaxUnits ? units - u0 : kWideMaxUnits;
-    hipLaunchKernelGGL((quest_score_wide_kernel<D, NT, 4>), dim3(256), dim3(kWideWaves * 64), 0, st, a, G, L.hkv, L.ps,
-                       L.hs, L.ts, u0, nu);
+    hipLaunchKernelGGL((quest_score_wide_kernel<D, NT, 3, kWideWaves>), dim3(256), dim3(kWideWaves * 64), 0, st, a, G,
+                       L.hkv, L.ps, L.hs, L.ts, u0, nu);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -60,9 +60,10 @@ struct DecodeShape {
 // final merge of the waves that share a head group.
 template <int G, int DK, int DV, bool VISK>
 __global__ __launch_bounds__((DecodeShape<G, DK, DV>::NW * 64))
-__attribute__((amdgpu_waves_per_eu(DK <= 128 ? 4 : 2))) void decode_kernel(DecodeArgs a, int Hkv, int64_t ps,
-                                                                                    int64_t hs, int64_t ts, int pps,
-                                                                                    float scale2) {
+__attribute__((amdgpu_waves_per_eu(DK > 128 ? 2 : G == 16 ? 3 : 4))) void decode_kernel(DecodeArgs a, int Hkv,
+                                                                                        int64_t ps, int64_t hs,
+                                                                                        int64_t ts, int pps,
+                                                                                        float scale2) {
   using S = DecodeShape<G, DK, DV>;
   constexpr int HW = S::HW, WPG = S::WPG, NW = S::NW, LPT = S::LPT, TPI = S::TPI, NTG = S::NTG, NCK = S::NCK;
   constexpr int LPV = S::LPV, TPV = S::TPV, NTV = S::NTV, PPS = S::PPS, PPW = S::PPW, LPH = S::LPH;

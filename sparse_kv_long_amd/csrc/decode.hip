@@ -965,10 +965,14 @@ int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, 
   const int target = mla_decode_shape(L, G) ? kMlaTargetBlocks / ((G + kMlaHeadsPerBlock - 1) / kMlaHeadsPerBlock)
                      : mfma_decode_shape(L, G) ? 512 : 1024;
   int s = requested > 0 ? requested : (target + units - 1) / units;
-  // the matrix-core GQA decode keeps at least 32 pages (8 per wave) per split:
-  // fewer leave every block with more fixed cost than streaming (measured at
-  // 32K, 128 kept pages: 23.0 us with 4 splits, 28.5 us with 8)
-  if (requested <= 0 && mfma_decode_shape(L, G) && s > kmax / 32) s = kmax / 32 > 0 ? kmax / 32 : 1;
+  // the matrix-core GQA decode keeps at least 32 pages (8 per wave) per split
+  // while that still gives every CU a block: fewer leave each block with more
+  // fixed cost than streaming (measured at 32K, 128 kept pages: 23.0 us with 4
+  // splits, 28.5 us with 8)
+  if (requested <= 0 && mfma_decode_shape(L, G)) {
+    const int s32 = kmax / 32 > 0 ? kmax / 32 : 1;
+    if ((int64_t)units * s32 >= 256 && s > s32) s = s32;
+  }
   if (s < smin) s = smin;
   if (s > kmax) s = kmax;
   if (s > kMaxSplits) s = kMaxSplits;

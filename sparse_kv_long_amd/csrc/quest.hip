@@ -544,14 +544,16 @@ void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs
 static int pick_ppw(int B, int Hkv, int MP) {
   // about 3072 waves: 768 blocks, the three per CU that the matrix-core
   // kernel's LDS allows, all resident at once (measured: fewer waves leave
-  // HBM idle, a second round of blocks costs more than it hides), but at
-  // least 96 pages each, so that short contexts do not pay a wave's fixed
-  // costs (ids, q, ring fill) for a handful of pages (measured at 32K: 23 us
-  // at 96 pages per wave against 26 us at 64); at most kMaxPagesPerWave
+  // HBM idle, a second round of blocks costs more than it hides), but, while
+  // that still leaves 1024 waves, at least 96 pages each, so that short
+  // contexts do not pay a wave's fixed costs (ids, q, ring fill) for a handful
+  // of pages (measured at 32K: 23 us at 96 pages per wave against 26 us at
+  // 64); at most kMaxPagesPerWave
   const int64_t pages = (int64_t)B * Hkv * MP;
   int64_t ppw = (pages + 3071) / 3072;
+  const int64_t floor_ppw = (pages + 1023) / 1024 < 96 ? (pages + 1023) / 1024 : 96;
+  if (ppw < floor_ppw) ppw = floor_ppw;
   ppw = (ppw + 31) / 32 * 32;
-  if (ppw < 96) ppw = 96;
   if (ppw > kMaxPagesPerWave) ppw = kMaxPagesPerWave;
   return (int)ppw;
 }

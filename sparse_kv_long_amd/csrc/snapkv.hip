@@ -257,7 +257,10 @@ __global__ __launch_bounds__(256) void snap_votes_kernel(SnapArgs a, const float
   const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + g) * a.N * D;
   float* vrow = votes + (((int64_t)rg * a.B + b) * a.Hkv + g) * a.N;
   const int tiles = (L + 31) / 32;
-  for (int kt = slot; kt < tiles; kt += slots) {
+  // the slot's tiles in descending order: pass 1 read them ascending, so the
+  // ones it read last (the likeliest still in the caches) come first
+  const int kt_last = slot < tiles ? slot + (tiles - 1 - slot) / slots * slots : -1;
+  for (int kt = kt_last; kt >= 0; kt -= slots) {
     uint4 kf[D / 16];
     load_k_frags<D>(kbase, kt, n, kf);
     float vote = 0.f;

@@ -210,6 +210,26 @@ def test_large_logit_range_matches_oracle(name):
     check_attention(to_np(out), ref, vmax, f"{name} q*16")
 
 
+def test_mla_batch_beyond_one_scorer_launch():
+    """2100 MLA units: more than one launch of the wide scorer's unit limit, each
+    with its own last-page refreshes; selection and attention of every unit
+    against the oracle."""
+    wl = QuestWorkload("t_mla_many", 2100, 8, 1, 576, 512, 80, 2, "none", v_is_k_prefix=True, ragged_lo=17, seed=23)
+    announce(f"mla many units seed {wl.seed}")
+    x = make_quest_inputs(wl, DEV, poison_tail=True)
+    summ = build_summaries(x, wl)
+    out, sel = run_sparse_decode(x, wl, summ, refresh=1)
+    h = host_inputs(x)
+    ref_summ = oracle.quest_summaries(h["k"], h["pt"], h["lens"])
+    A = oracle.quest_scores(h["q"], ref_summ, h["lens"], wl.group, wl.scale)
+    sel_np = to_np(sel)
+    for b, n in enumerate(h["lens"]):
+        check_selection(sel_np[b, 0], A[b, 0, :-(-int(n) // 16)], wl.topk, f"mla many b{b}")
+    ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], sel_lists(sel_np, h["lens"]), wl.group,
+                                  wl.scale, wl.head_dim_v, wl.v_is_k_prefix)
+    check_attention(to_np(out), ref, float(torch.nan_to_num(x["k_pages"], 0.0).abs().max()), "mla many")
+
+
 def test_empty_and_single_token_requests():
     wl = QuestWorkload("t_edge", 4, 8, 2, 128, 128, 64, 2, "none", seed=21)
     announce("edge lengths [0, 1, 16, 17]")

@@ -22,7 +22,8 @@ Table 7):
       of s * q.k over the page's keys.
   O3  KV-head score: max of U over the query heads that share the KV head.
   O4  selection: the min(topk, pages) pages with the largest score, ties to
-      the lower page id, returned ascending.
+      the lower page id, returned ascending; optionally with always-kept sink
+      and recent pages beside the selected budget (appendix Tables 8-11).
   O5  attention: softmax attention of each query head over the valid tokens
       of its KV head's selected pages (Table 7: logit z, weight alpha).
   O6  SnapKV: window-row softmax over each row's causal history (Table 7:
@@ -128,6 +129,25 @@ def unit_select(scores: np.ndarray, topk: int) -> np.ndarray:
     return np.array(sorted(order[:k]), dtype=np.int64)
 
 
+def unit_select_forced(scores: np.ndarray, topk: int, sink: int, recent: int) -> np.ndarray:
+    """O4 with always-kept pages: the first ``sink`` and the last ``recent``
+    pages of the request, plus the ``topk`` pages of largest score among the
+    others (ties to the lower id), ascending.
+
+    SparseEngine appendix Tables 8-11 list a Sink and a Recent budget beside
+    each method's selected budget, and Table 10's caption says the selected
+    budget excludes them (Quest there: 64 sink + 512 recent + 1,472 selected
+    = 2,048 tokens); the StreamingLLM rows have sink and recent only, which is
+    topk = 0 here.  Budgets are in pages (16 tokens each).
+    """
+    P = len(scores)
+    forced = set(range(min(int(sink), P))) | set(range(max(P - int(recent), 0), P))
+    rest = [p for p in range(P) if p not in forced]
+    ranked = sorted(rest, key=lambda p: (-float(scores[p]), p))
+    chosen = forced | set(ranked[:max(int(topk), 0)])
+    return np.array(sorted(chosen), dtype=np.int64)
+
+
 def unit_attention(q_heads: np.ndarray, keys: np.ndarray, vals: np.ndarray, scale: float) -> np.ndarray:
     """O5: out[h] = sum_t alpha[h,t] v_t with alpha = softmax_t(s * q_h . k_t).
 
@@ -221,13 +241,17 @@ def quest_scores(q, summaries, seq_lens, group: int, scale: float, page_size: in
     return A
 
 
-def quest_select(A, seq_lens, topk: int, page_size: int = PAGE):
-    """O4 for every (request, KV head): nested list of ascending id arrays."""
+def quest_select(A, seq_lens, topk: int, page_size: int = PAGE, sink: int = 0, recent: int = 0):
+    """O4 for every (request, KV head): nested list of ascending id arrays
+    (with always-kept sink and recent pages when either is non-zero)."""
     B, Hkv, _ = A.shape
     out = []
     for b in range(B):
         P = pages_of(seq_lens[b], page_size)
-        out.append([unit_select(A[b, g, :P], topk) for g in range(Hkv)])
+        if sink or recent:
+            out.append([unit_select_forced(A[b, g, :P], topk, sink, recent) for g in range(Hkv)])
+        else:
+            out.append([unit_select(A[b, g, :P], topk) for g in range(Hkv)])
     return out
 
 
@@ -254,11 +278,12 @@ def sparse_attention(q, k_pages, v_pages, page_table, seq_lens, selection, group
 
 
 def sparse_decode(q, k_pages, v_pages, page_table, seq_lens, topk: int, group: int, scale: float,
-                  head_dim_v: int, v_is_k_prefix: bool = False, page_size: int = PAGE, mode: str = "max"):
+                  head_dim_v: int, v_is_k_prefix: bool = False, page_size: int = PAGE, mode: str = "max",
+                  sink: int = 0, recent: int = 0):
     """The whole Quest decode step O1-O5.  Returns (out, selection, scores)."""
     summ = quest_summaries(k_pages, page_table, seq_lens, page_size)
     A = quest_scores(q, summ, seq_lens, group, scale, page_size, mode)
-    sel = quest_select(A, seq_lens, topk, page_size)
+    sel = quest_select(A, seq_lens, topk, page_size, sink, recent)
     out = sparse_attention(q, k_pages, v_pages, page_table, seq_lens, sel, group, scale, head_dim_v,
                            v_is_k_prefix, page_size)
     return out, sel, A

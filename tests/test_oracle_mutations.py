@@ -31,6 +31,9 @@ def _pins():
         lambda: tq.test_selection_against_pairwise_order.hypothesis.inner_test(seed=5, P=40, topk=9, levels=3),
         lambda: tq.test_selection_against_pairwise_order.hypothesis.inner_test(seed=6, P=17, topk=30, levels=2),
         lambda: tq.test_dense_case_equals_library_attention(4, 64, (100, 1)),
+        tq.test_forced_selection_special_cases,
+        lambda: tq.test_forced_selection_against_its_definition.hypothesis.inner_test(seed=12, P=23, topk=4, sink=2,
+                                                                                      recent=3, levels=3),
         tq.test_sparse_output_is_convex_combination_of_selected_rows,
         tq.test_split_merge_equals_single_softmax,
         ts.test_worked_example_w2,
@@ -85,6 +88,20 @@ def select_one_short(scores, topk):
     P = len(scores)
     order = sorted(range(P), key=lambda p: (-float(scores[p]), p))
     return np.array(sorted(order[:max(min(topk, P) - 1, 0)]), dtype=np.int64)
+
+
+def forced_inside_budget(scores, topk, sink, recent):
+    P = len(scores)
+    forced = set(range(min(sink, P))) | set(range(max(P - recent, 0), P))
+    rest = sorted((p for p in range(P) if p not in forced), key=lambda p: (-float(scores[p]), p))
+    return np.array(sorted(forced | set(rest[:max(topk - len(forced), 0)])), dtype=np.int64)
+
+
+def forced_recent_one_short(scores, topk, sink, recent):
+    P = len(scores)
+    forced = set(range(min(sink, P))) | set(range(max(P - recent + 1, 0), P))
+    rest = sorted((p for p in range(P) if p not in forced), key=lambda p: (-float(scores[p]), p))
+    return np.array(sorted(forced | set(rest[:topk])), dtype=np.int64)
 
 
 def summaries_over_whole_last_page(keys_pages, n, page_size=PAGE):
@@ -206,6 +223,8 @@ MUTANTS = {
     "select: ties to higher id": ("unit_select", select_ties_to_higher_id),
     "select: score order": ("unit_select", select_in_score_order),
     "select: one short": ("unit_select", select_one_short),
+    "forced: pages counted inside the budget": ("unit_select_forced", forced_inside_budget),
+    "forced: recent one page short": ("unit_select_forced", forced_recent_one_short),
     "summaries: whole last page": ("unit_summaries", summaries_over_whole_last_page),
     "summaries: last valid token dropped": ("unit_summaries", summaries_drop_last_valid_token),
     "attention: missing scale": ("unit_attention", attention_without_scale),

@@ -181,6 +181,47 @@ def test_selection_against_pairwise_order(seed, P, topk, levels):
                 assert scores[i] > scores[j] or (scores[i] == scores[j] and i < j)
 
 
+@settings(max_examples=60, deadline=None)
+@given(seed=st.integers(0, 10_000), P=st.integers(1, 40), topk=st.integers(0, 20), sink=st.integers(0, 6),
+       recent=st.integers(0, 9), levels=st.integers(1, 5))
+def test_forced_selection_against_its_definition(seed, P, topk, sink, recent, levels):
+    """Sink and recent pages beside the selected budget (appendix Tables 8-11):
+    the first `sink` and last `recent` pages are always kept, and among the
+    other pages exactly min(topk, #others) are kept, each beating every dropped
+    one (higher score, or equal score and lower id)."""
+    rng = np.random.default_rng(seed)
+    scores = rng.integers(0, levels, P).astype(np.float64) - 1.5  # many exact ties
+    sel = oracle.unit_select_forced(scores, topk, sink, recent)
+    assert (np.diff(sel) > 0).all()
+    kept = set(sel.tolist())
+    forced = {p for p in range(P) if p < sink or p >= P - recent}
+    assert forced <= kept
+    others = [p for p in range(P) if p not in forced]
+    picked = kept - forced
+    assert len(picked) == min(topk, len(others))
+    for i in picked:
+        for j in others:
+            if j not in kept:
+                assert scores[i] > scores[j] or (scores[i] == scores[j] and i < j)
+
+
+def test_forced_selection_special_cases():
+    rng = np.random.default_rng(31)
+    for P in (1, 5, 17, 64):
+        scores = rng.normal(size=P)
+        # no forced pages: plain top-k
+        for k in (1, 3, 70):
+            assert oracle.unit_select_forced(scores, k, 0, 0).tolist() == oracle.unit_select(scores, k).tolist()
+        # StreamingLLM: sink and recent only, no scoring budget
+        assert oracle.unit_select_forced(scores, 0, 2, 3).tolist() == sorted(set(range(min(2, P))) |
+                                                                                set(range(max(P - 3, 0), P)))
+        # a budget covering the request keeps every page
+        assert oracle.unit_select_forced(scores, P, 1, 1).tolist() == list(range(P))
+    # worked case: 10 pages, sink 1, recent 2, budget 3 among pages 1..7
+    scores = np.array([0.0, 5.0, 1.0, 7.0, 7.0, 2.0, 9.0, 3.0, -1.0, -2.0])
+    assert oracle.unit_select_forced(scores, 3, 1, 2).tolist() == [0, 3, 4, 6, 8, 9]
+
+
 @pytest.mark.parametrize("G,D,lens", [(1, 8, (37, 16)), (4, 64, (100, 1)), (8, 16, (200, 129))])
 def test_dense_case_equals_library_attention(G, D, lens):
     rng = np.random.default_rng(G * 100 + D)

@@ -83,15 +83,28 @@ typedef struct se_decode_params {
   int32_t batch;              /* B                                            */
   int32_t num_q_heads;        /* Hq, a multiple of Hkv; G = Hq/Hkv <= 32      */
   int32_t max_pages_per_seq;  /* row length of page_table (<= 65536)          */
-  int32_t topk;               /* pages kept per (request, KV head), >= 1.
-                                 Request b runs dense when topk >= its pages. */
+  int32_t topk;               /* pages selected by score per (request, KV
+                                 head), >= 0, beside the forced pages below.
+                                 Request b runs dense when
+                                 topk + sink_pages + recent_pages >= its pages. */
   float sm_scale;             /* softmax scale s; 0 means 1/sqrt(Dk)          */
   int32_t head_agg;           /* 0: page score = max over the KV head's query
                                  heads (default); 1: sum                      */
   int32_t refresh_last_page;  /* 1: recompute the summary of each request's
                                  last page from its keys before scoring      */
   int32_t num_splits;         /* split-K factor of the attention; 0 = auto    */
+  int32_t sink_pages;         /* >= 0: the first sink_pages pages of every
+                                 request are always kept                      */
+  int32_t recent_pages;       /* >= 0: the last recent_pages pages of every
+                                 request are always kept                      */
 } se_decode_params;
+/* Forced pages (SparseEngine appendix Tables 8-11: a sink and a recent budget
+ * beside each method's selected budget, which excludes them; the StreamingLLM
+ * rows keep sink and recent only).  A request keeps its forced pages plus the
+ * topk best-scoring others, at most kcap = topk + sink_pages + recent_pages
+ * pages; `selected` arrays are [B, Hkv, kcap].  topk = 0 is StreamingLLM: no
+ * page is scored, `summaries` is not read (may be NULL) and refresh_last_page
+ * must be 0.  kcap must be >= 1; each count <= 65536. */
 
 /* Version as major*10000 + minor*100 + patch. */
 int se_version(void);
@@ -125,19 +138,20 @@ int se_build_summaries(const se_kv_layout* layout, int32_t batch, int32_t max_pa
  *   page_table  int32 [B, max_pages_per_seq]
  *   summaries   bf16 [P, Hkv, 2, Dk]; read, and with refresh_last_page the
  *               last page of each request is rewritten.  May be NULL only
- *               when topk >= max_pages_per_seq and refresh_last_page = 0.
+ *               when refresh_last_page = 0 and either topk = 0 or
+ *               kcap >= max_pages_per_seq.
  *   seq_lens    int32 [B]; counts the current token, whose K/V the caller
  *               has already appended.  0 gives a zero output row.
  *   out         fp32 [B, Hq, Dv]
- *   selected    int32 [B, Hkv, topk] or NULL; receives each KV head's kept
+ *   selected    int32 [B, Hkv, kcap] or NULL; receives each KV head's kept
  *               logical page ids in ascending order, padded with -1.
  *   workspace   device scratch of at least se_sparse_decode_workspace_size
  *               bytes, 256-byte aligned; contents need no initialisation.
  *
  * Steps: page scores (U = s * sum_c max(q_c*min_c, q_c*max_c) per query
  * head, reduced to the KV head), top-k per KV head (ties to the lower page
- * id), split-K softmax attention over the kept pages' valid tokens, and a
- * log-sum-exp merge of the splits.
+ * id) beside the forced sink and recent pages, split-K softmax attention over
+ * the kept pages' valid tokens, and a log-sum-exp merge of the splits.
  * ------------------------------------------------------------------------- */
 int se_sparse_decode_workspace_size(const se_kv_layout* layout, const se_decode_params* params,
                                     size_t* bytes);
@@ -156,11 +170,12 @@ int se_quest_scores(const se_kv_layout* layout, const se_decode_params* params, 
                     const void* k_pages, const int32_t* page_table, void* summaries,
                     const int32_t* seq_lens, float* scores, void* stream);
 
-/* selected: int32 [B, Hkv, topk] from scores laid out as above. */
+/* selected: int32 [B, Hkv, kcap] from scores laid out as above (scores are
+ * not read when topk = 0). */
 int se_topk_pages(const se_decode_params* params, int32_t num_kv_heads, const float* scores,
                   const int32_t* seq_lens, int32_t* selected, void* stream);
 
-/* Attention over the pages listed in `selected` ([B, Hkv, topk], ascending,
+/* Attention over the pages listed in `selected` ([B, Hkv, kcap], ascending,
  * -1 padded), or over every page of each request when `selected` is NULL.
  * workspace as for se_sparse_decode. */
 int se_decode_selected(const se_kv_layout* layout, const se_decode_params* params, const void* q,

@@ -42,7 +42,8 @@ class DecodeParams(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("max_pages_per_seq", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float), ("head_agg", ctypes.c_int32),
-                ("refresh_last_page", ctypes.c_int32), ("num_splits", ctypes.c_int32)]
+                ("refresh_last_page", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("sink_pages", ctypes.c_int32), ("recent_pages", ctypes.c_int32)]
 
 
 class SnapKVParams(ctypes.Structure):
@@ -138,9 +139,14 @@ def dense_layout(num_kv_heads: int, capacity: int, head_dim: int) -> KvLayout:
 
 
 def decode_params(batch, num_q_heads, max_pages_per_seq, topk, sm_scale=0.0, head_agg=0,
-                  refresh_last_page=0, num_splits=0) -> DecodeParams:
+                  refresh_last_page=0, num_splits=0, sink_pages=0, recent_pages=0) -> DecodeParams:
     return DecodeParams(batch, num_q_heads, max_pages_per_seq, topk, sm_scale, head_agg, refresh_last_page,
-                        num_splits)
+                        num_splits, sink_pages, recent_pages)
+
+
+def kept_capacity(params: DecodeParams) -> int:
+    """Last dimension of `selected` arrays: topk + sink_pages + recent_pages."""
+    return params.topk + params.sink_pages + params.recent_pages
 
 
 def snapkv_params(batch, num_q_heads, num_kv_heads, head_dim, max_prompt_len, window, pool_kernel, budget,

@@ -12,7 +12,7 @@ namespace {
 
 using se::Layout;
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: forced sink and recent pages
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -46,9 +46,21 @@ Layout to_layout(const se_kv_layout* L) {
   return o;
 }
 
+// pages a (request, KV head) keeps at most: the selected budget plus the forced pages
+int kept_cap(const se_decode_params* p) { return p->topk + p->sink_pages + p->recent_pages; }
+
+int check_counts(const se_decode_params* p) {
+  if (p->topk < 0 || p->sink_pages < 0 || p->recent_pages < 0) return SE_EINVAL;
+  if (p->topk > 65536 || p->sink_pages > 65536 || p->recent_pages > 65536) return SE_EUNSUPPORTED;
+  if (kept_cap(p) < 1) return SE_EINVAL;
+  if (p->topk == 0 && p->refresh_last_page) return SE_EINVAL;  // nothing is scored, so nothing to refresh for
+  return SE_OK;
+}
+
 int check_params(const se_kv_layout* L, const se_decode_params* p) {
   if (!p) return SE_EINVAL;
-  if (p->batch < 0 || p->num_q_heads < 1 || p->topk < 1 || p->max_pages_per_seq < 1) return SE_EINVAL;
+  if (p->batch < 0 || p->num_q_heads < 1 || p->max_pages_per_seq < 1) return SE_EINVAL;
+  if (const int rc = check_counts(p)) return rc;
   if (p->num_q_heads % L->num_kv_heads) return SE_EINVAL;
   if (!pow2_group(p->num_q_heads / L->num_kv_heads)) return SE_EUNSUPPORTED;
   if (p->max_pages_per_seq > 65536) return SE_EUNSUPPORTED;
@@ -72,13 +84,13 @@ DecodeWs decode_ws(const se_kv_layout* L, const se_decode_params* p, bool dense)
   const Layout l = to_layout(L);
   DecodeWs w;
   const int B = p->batch, Hkv = L->num_kv_heads, MP = p->max_pages_per_seq;
-  w.splits = se::decode_splits(l, B, p->num_q_heads, MP, p->topk, dense, p->num_splits);
-  const int s_other = se::decode_splits(l, B, p->num_q_heads, MP, p->topk, !dense, p->num_splits);
+  w.splits = se::decode_splits(l, B, p->num_q_heads, MP, kept_cap(p), dense, p->num_splits);
+  const int s_other = se::decode_splits(l, B, p->num_q_heads, MP, kept_cap(p), !dense, p->num_splits);
   const int smax = w.splits > s_other ? w.splits : s_other;
   w.scores = 0;
   w.sel = w.scores + align256((size_t)B * Hkv * MP * sizeof(float));
-  w.phys = w.sel + align256((size_t)B * Hkv * p->topk * sizeof(int32_t));
-  w.acc = w.phys + align256((size_t)B * Hkv * p->topk * sizeof(int32_t));
+  w.phys = w.sel + align256((size_t)B * Hkv * kept_cap(p) * sizeof(int32_t));
+  w.acc = w.phys + align256((size_t)B * Hkv * kept_cap(p) * sizeof(int32_t));
   w.ml = w.acc + align256((size_t)B * p->num_q_heads * smax * L->head_dim_v * sizeof(float));
   w.total = w.ml + align256((size_t)B * p->num_q_heads * smax * 2 * sizeof(float));
   return w;
@@ -158,7 +170,7 @@ int se_sparse_decode_workspace_size(const se_kv_layout* layout, const se_decode_
   rc = check_params(layout, params);
   if (rc) return rc;
   if (!bytes) return SE_EINVAL;
-  *bytes = decode_ws(layout, params, params->topk >= params->max_pages_per_seq).total;
+  *bytes = decode_ws(layout, params, kept_cap(params) >= params->max_pages_per_seq).total;
   return SE_OK;
 }
 
@@ -181,8 +193,10 @@ int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params,
   if (params->batch == 0) return SE_OK;
   rc = check_decode_ptrs(layout, q, k_pages, v_pages, page_table, seq_lens, out);
   if (rc) return rc;
-  const bool all_dense = params->topk >= params->max_pages_per_seq;
-  const bool need_scores = !all_dense || params->refresh_last_page;
+  const int kcap = kept_cap(params);
+  const bool all_dense = kcap >= params->max_pages_per_seq;
+  // topk = 0 (sink and recent pages only) scores nothing
+  const bool need_scores = (!all_dense && params->topk > 0) || params->refresh_last_page;
   if (need_scores && (!summaries || !aligned16(summaries))) return SE_EINVAL;
   const DecodeWs w = decode_ws(layout, params, all_dense);
   if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return SE_EWORKSPACE;
@@ -206,7 +220,7 @@ int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params,
     a.B = params->batch;
     a.Hq = params->num_q_heads;
     a.MP = params->max_pages_per_seq;
-    a.topk = params->topk;
+    a.topk = kcap;  // a request with kcap >= its pages runs dense and is not scored
     a.refresh = params->refresh_last_page;
     a.head_sum = params->head_agg;
     a.scale = scale;
@@ -214,8 +228,9 @@ int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params,
     if (rc) return rc;
   }
   if (!all_dense || selected) {
-    rc = hip_status(se::launch_topk_pages(params->batch, L.hkv, params->max_pages_per_seq, params->topk, scores,
-                                          seq_lens, sel, page_table, all_dense ? nullptr : phys, st));
+    rc = hip_status(se::launch_topk_pages(params->batch, L.hkv, params->max_pages_per_seq, params->topk,
+                                          params->sink_pages, params->recent_pages, scores, seq_lens, sel, page_table,
+                                          all_dense ? nullptr : phys, st));
     if (rc) return rc;
   }
   se::DecodeArgs d;
@@ -232,7 +247,7 @@ int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params,
   d.B = params->batch;
   d.Hq = params->num_q_heads;
   d.MP = params->max_pages_per_seq;
-  d.topk = params->topk;
+  d.topk = kcap;  // row length of the selection
   d.splits = w.splits;
   d.scale = scale;
   return hip_status(se::launch_decode(L, d, st));
@@ -258,7 +273,7 @@ int se_quest_scores(const se_kv_layout* layout, const se_decode_params* params, 
   a.B = params->batch;
   a.Hq = params->num_q_heads;
   a.MP = params->max_pages_per_seq;
-  a.topk = params->topk;
+  a.topk = kept_cap(params);  // a request with kcap >= its pages runs dense and is not scored
   a.refresh = params->refresh_last_page;
   a.head_sum = params->head_agg;
   a.scale = eff_scale(layout, params);
@@ -268,12 +283,14 @@ int se_quest_scores(const se_kv_layout* layout, const se_decode_params* params, 
 int se_topk_pages(const se_decode_params* params, int32_t num_kv_heads, const float* scores, const int32_t* seq_lens,
                   int32_t* selected, void* stream) {
   if (!params || num_kv_heads < 1) return SE_EINVAL;
-  if (params->batch < 0 || params->topk < 1 || params->max_pages_per_seq < 1) return SE_EINVAL;
+  if (params->batch < 0 || params->max_pages_per_seq < 1) return SE_EINVAL;
+  if (const int rc = check_counts(params)) return rc;
   if (params->max_pages_per_seq > 65536) return SE_EUNSUPPORTED;
   if (params->batch == 0) return SE_OK;
-  if (!scores || !seq_lens || !selected) return SE_EINVAL;
-  return hip_status(se::launch_topk_pages(params->batch, num_kv_heads, params->max_pages_per_seq, params->topk, scores,
-                                          seq_lens, selected, nullptr, nullptr, (hipStream_t)stream));
+  if ((params->topk > 0 && !scores) || !seq_lens || !selected) return SE_EINVAL;
+  return hip_status(se::launch_topk_pages(params->batch, num_kv_heads, params->max_pages_per_seq, params->topk,
+                                          params->sink_pages, params->recent_pages, scores, seq_lens, selected,
+                                          nullptr, nullptr, (hipStream_t)stream));
 }
 
 int se_decode_selected(const se_kv_layout* layout, const se_decode_params* params, const void* q, const void* k_pages,
@@ -304,7 +321,7 @@ int se_decode_selected(const se_kv_layout* layout, const se_decode_params* param
   d.B = params->batch;
   d.Hq = params->num_q_heads;
   d.MP = params->max_pages_per_seq;
-  d.topk = params->topk;
+  d.topk = kept_cap(params);  // row length of the selection
   d.splits = w.splits;
   d.scale = eff_scale(layout, params);
   return hip_status(se::launch_decode(to_layout(layout), d, (hipStream_t)stream));

@@ -28,9 +28,13 @@ struct ScoreArgs {
 };
 hipError_t launch_quest_scores(const Layout& L, const ScoreArgs& a, hipStream_t st);
 
-// phys (nullable): also write page_table[b][id] for every selected id
-hipError_t launch_topk_pages(int B, int Hkv, int MP, int topk, const float* scores, const int32_t* seq_lens,
-                             int32_t* selected, const int32_t* page_table, int32_t* phys, hipStream_t st);
+// Per (request, KV head): the first `sink` and last `recent` pages plus the
+// `topk` best-scoring others; selected rows hold topk + sink + recent ids.
+// phys (nullable): also write page_table[b][id] for every selected id.
+// scores is not read when topk = 0.
+hipError_t launch_topk_pages(int B, int Hkv, int MP, int topk, int sink, int recent, const float* scores,
+                             const int32_t* seq_lens, int32_t* selected, const int32_t* page_table, int32_t* phys,
+                             hipStream_t st);
 
 struct DecodeArgs {
   const uint16_t* q;

@@ -95,11 +95,14 @@ __device__ __forceinline__ void block_and_or(uint32_t& vand, uint32_t& vor, Topk
 }
 
 // Requires 0 < k < N <= KPT * 1024.  Writes k indices into out[0..k) and,
-// when `translate` is given, translate[index] into out2[0..k).
+// when `translate` is given, translate[index] into out2[0..k).  Indices below
+// `forced_lo` or from `forced_hi` on take the largest key, so they are always
+// kept (their number must not exceed k).
 template <int KPT>
 __device__ __forceinline__ void block_topk(const float* __restrict__ row, int N, int k, int32_t* __restrict__ out,
                                            TopkShared& sm,
-                           const int32_t* __restrict__ translate = nullptr, int32_t* __restrict__ out2 = nullptr) {
+                           const int32_t* __restrict__ translate = nullptr, int32_t* __restrict__ out2 = nullptr,
+                           int forced_lo = 0, int forced_hi = 0x7fffffff) {
   const int tid = threadIdx.x;
   const int base = tid * KPT;
   uint32_t key[KPT];
@@ -124,6 +127,9 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ row, int N,
 #pragma unroll
     for (int i = 0; i < KPT; ++i) tr[i] = (base + i < N) ? translate[base + i] : 0;
   }
+#pragma unroll
+  for (int i = 0; i < KPT; ++i)
+    if (base + i < forced_lo || base + i >= forced_hi) key[i] = 0xffffffffu;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
     if (base + i < N) {
@@ -236,8 +242,9 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ row, int N,
 }
 
 // ---------------------------------------------------------------------------
-// Quest: pages of (b, g).  P = ceil(seq_len/16); k' = min(topk, P); output
-// [B, Hkv, topk] ascending, padded with -1.
+// Quest: pages of (b, g).  P = ceil(seq_len/16).  Forced pages: [0, s) and
+// [r_lo, P) with s = min(sink, P), r_lo = max(P - recent, s); the row holds
+// kk = min(cap, P) ids (cap = topk + sink + recent), ascending, padded with -1.
 // ---------------------------------------------------------------------------
 template <int KPT>
 __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(const float* __restrict__ scores,
@@ -245,16 +252,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(const float* _
                                                                   int32_t* __restrict__ selected,
                                                                   const int32_t* __restrict__ page_table,
                                                                   int32_t* __restrict__ phys, int Hkv, int MP,
-                                                                  int topk) {
+                                                                  int topk, int sink, int recent) {
   __shared__ TopkShared sm;
   const int b = blockIdx.y, g = blockIdx.x;
   const int n = seq_lens[b];
   const int P = (n + kPage - 1) / kPage;
-  const int kk = min(topk, P);
-  int32_t* out = selected + ((int64_t)b * Hkv + g) * topk;
-  int32_t* out2 = phys ? phys + ((int64_t)b * Hkv + g) * topk : nullptr;
+  const int cap = topk + sink + recent;
+  const int kk = min(cap, P);
+  int32_t* out = selected + ((int64_t)b * Hkv + g) * cap;
+  int32_t* out2 = phys ? phys + ((int64_t)b * Hkv + g) * cap : nullptr;
   const int32_t* ptrow = page_table ? page_table + (int64_t)b * MP : nullptr;
-  for (int i = kk + threadIdx.x; i < topk; i += blockDim.x) {
+  for (int i = kk + threadIdx.x; i < cap; i += blockDim.x) {
     out[i] = -1;
     if (out2) out2[i] = -1;
   }
@@ -265,7 +273,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(const float* _
     }
     return;
   }
-  block_topk<KPT>(scores + ((int64_t)b * Hkv + g) * MP, P, kk, out, sm, ptrow, out2);
+  const int s_end = min(sink, P), r_lo = max(P - recent, s_end);
+  const int nforced = s_end + (P - r_lo);
+  if (kk == nforced) {  // no selected budget (topk = 0): the forced pages alone, no scores read
+    for (int i = threadIdx.x; i < kk; i += blockDim.x) {
+      const int p = i < s_end ? i : r_lo + (i - s_end);
+      out[i] = p;
+      if (out2) out2[i] = ptrow[p];
+    }
+    return;
+  }
+  block_topk<KPT>(scores + ((int64_t)b * Hkv + g) * MP, P, kk, out, sm, ptrow, out2, s_end, r_lo);
 }
 
 static int pick_kpt(int n) {
@@ -274,15 +292,16 @@ static int pick_kpt(int n) {
   return kpt;
 }
 
-hipError_t launch_topk_pages(int B, int Hkv, int MP, int topk, const float* scores, const int32_t* seq_lens,
-                             int32_t* selected, const int32_t* page_table, int32_t* phys, hipStream_t st) {
+hipError_t launch_topk_pages(int B, int Hkv, int MP, int topk, int sink, int recent, const float* scores,
+                             const int32_t* seq_lens, int32_t* selected, const int32_t* page_table, int32_t* phys,
+                             hipStream_t st) {
   if (B == 0) return hipSuccess;
   dim3 grid(Hkv, B);
   switch (pick_kpt(MP)) {
 #define SE_K(K)                                                                                                    \
   case K:                                                                                                          \
     hipLaunchKernelGGL(topk_pages_kernel<K>, grid, dim3(kTopkThreads), 0, st, scores, seq_lens, selected,         \
-                       page_table, phys, Hkv, MP, topk);                                                           \
+                       page_table, phys, Hkv, MP, topk, sink, recent);                                             \
     break;
     SE_K(1) SE_K(2) SE_K(4) SE_K(8) SE_K(16) SE_K(32) SE_K(64)
 #undef SE_K

@@ -49,21 +49,21 @@ def build_summaries(x, wl):
     return summ
 
 
-def params_for(wl, topk=None, refresh=1, splits=0, head_agg=0):
+def params_for(wl, topk=None, refresh=1, splits=0, head_agg=0, sink=0, recent=0):
     return se.decode_params(wl.batch, wl.num_q_heads, wl.max_pages, wl.topk if topk is None else topk, wl.scale,
-                            head_agg, refresh, splits)
+                            head_agg, refresh, splits, sink, recent)
 
 
 def workspace(nbytes):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
 
 
-def run_sparse_decode(x, wl, summ, topk=None, refresh=1, splits=0, head_agg=0):
-    P = params_for(wl, topk, refresh, splits, head_agg)
+def run_sparse_decode(x, wl, summ, topk=None, refresh=1, splits=0, head_agg=0, sink=0, recent=0):
+    P = params_for(wl, topk, refresh, splits, head_agg, sink, recent)
     L = layout_for(wl)
     ws = workspace(se.se_sparse_decode_workspace_size(L, P))
     out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim_v), dtype=torch.float32, device=DEV)
-    sel = torch.empty((wl.batch, wl.num_kv_heads, P.topk), dtype=torch.int32, device=DEV)
+    sel = torch.empty((wl.batch, wl.num_kv_heads, se.kept_capacity(P)), dtype=torch.int32, device=DEV)
     se.se_sparse_decode(L, P, x["q"], x["k_pages"], x["v_pages"], x["page_table"], summ, x["seq_lens"], out, sel, ws)
     torch.cuda.synchronize()
     return out, sel
@@ -105,6 +105,30 @@ def check_selection(sel_row, scores, topk, what=""):
     kept = set(ids.tolist())
     assert set(must.tolist()) <= kept, f"{what}: missing ids above the gap"
     assert (scores[ids] >= tau - eps).all(), f"{what}: ids below the gap"
+
+
+def check_forced_selection(sel_row, scores, topk, sink, recent, what=""):
+    """A selection with always-kept pages: the first `sink` and last `recent`
+    pages exactly, and among the other pages the gap rule for `topk`."""
+    P = len(scores)
+    cap = topk + sink + recent
+    got = np.asarray(sel_row)
+    forced = sorted({p for p in range(P) if p < sink or p >= P - recent})
+    others = np.array([p for p in range(P) if p not in set(forced)], dtype=np.int64)
+    k = min(cap, P)
+    ids = got[:k]
+    assert len(got) == cap and (got[k:] == -1).all(), f"{what}: padding"
+    assert (np.diff(ids) > 0).all() and ((ids >= 0) & (ids < P)).all(), f"{what}: not ascending ids in range"
+    assert set(forced) <= set(ids.tolist()), f"{what}: a forced page is missing"
+    picked = np.array(sorted(set(ids.tolist()) - set(forced)), dtype=np.int64)
+    assert len(picked) == min(topk, len(others)), f"{what}: wrong number of selected pages"
+    if len(picked) == 0 or len(picked) == len(others):
+        return
+    # gap rule among the non-forced pages, in their own index space
+    pos = {int(p): i for i, p in enumerate(others)}
+    row = np.full(topk, -1, dtype=np.int64)
+    row[:len(picked)] = [pos[int(p)] for p in picked]
+    check_selection(row, scores[others], topk, what)
 
 
 def check_attention(out_gpu, out_ref, vmax, what=""):

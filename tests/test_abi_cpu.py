@@ -27,7 +27,7 @@ def test_every_header_function_is_exported_and_wrapped(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert se.se_version() == 100
+    assert se.se_version() == 200
     assert se.se_status_string(0) == "ok"
     assert "invalid" in se.se_status_string(1)
     assert "unsupported" in se.se_status_string(2)
@@ -37,7 +37,7 @@ def test_version_and_status_strings(lib):
 
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(se.KvLayout) == 6 * 4 + 3 * 8
-    assert ctypes.sizeof(se.DecodeParams) == 8 * 4
+    assert ctypes.sizeof(se.DecodeParams) == 10 * 4
     assert ctypes.sizeof(se.SnapKVParams) == 10 * 4
 
 
@@ -69,7 +69,13 @@ def test_workspace_size_query():
     (lambda L, P: setattr(L, "num_kv_heads", 0), se.SE_EINVAL),
     (lambda L, P: setattr(P, "num_q_heads", 30), se.SE_EINVAL),
     (lambda L, P: setattr(P, "num_q_heads", 12), se.SE_EUNSUPPORTED),
-    (lambda L, P: setattr(P, "topk", 0), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "topk", -1), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "topk", 0), se.SE_EINVAL),  # no pages kept at all
+    (lambda L, P: setattr(P, "sink_pages", -1), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "recent_pages", -1), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "recent_pages", 70000), se.SE_EUNSUPPORTED),
+    (lambda L, P: (setattr(P, "topk", 0), setattr(P, "sink_pages", 1), setattr(P, "refresh_last_page", 1)),
+     se.SE_EINVAL),  # nothing is scored when topk = 0, so no refresh
     (lambda L, P: setattr(P, "batch", -1), se.SE_EINVAL),
     (lambda L, P: setattr(P, "max_pages_per_seq", 70000), se.SE_EUNSUPPORTED),
     (lambda L, P: setattr(P, "sm_scale", -1.0), se.SE_EINVAL),
@@ -106,6 +112,13 @@ def test_decode_misaligned_and_workspace():
     assert rc_decode(Lm, Pm, v=None, summ=None, nbytes=0) == se.SE_EWORKSPACE
     Pm.refresh_last_page = 1
     assert rc_decode(Lm, Pm, v=None, summ=None) == se.SE_EINVAL
+    # sink and recent pages only (topk = 0): summaries are not needed
+    Ps = se.decode_params(2, 32, 64, 0, sink_pages=1, recent_pages=4)
+    assert rc_decode(L, Ps, summ=None, nbytes=0) == se.SE_EWORKSPACE
+    need_s = se.se_sparse_decode_workspace_size(L, Ps)
+    need_k = se.se_sparse_decode_workspace_size(L, se.decode_params(2, 32, 64, 5))
+    assert need_s == need_k  # the same kept capacity, the same workspace
+    assert se.kept_capacity(Ps) == 5
     # an empty batch is a no-op
     P0 = se.decode_params(0, 32, 64, 8)
     assert rc_decode(L, P0, q=None, ws=None) == se.SE_OK

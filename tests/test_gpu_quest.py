@@ -8,7 +8,8 @@ import torch
 import oracle
 import sparse_kv_long_amd as se
 from synth import QuestWorkload, TINY_QUEST, make_quest_inputs, bf16_bits
-from gpu_util import (DEV, announce, build_summaries, check_attention, check_selection, host_inputs, layout_for,
+from gpu_util import (DEV, announce, build_summaries, check_attention, check_forced_selection, check_selection,
+                      host_inputs, layout_for,
                       params_for, run_sparse_decode, score_tolerance, sel_lists, to_np, workspace)
 
 pytestmark = pytest.mark.gpu
@@ -228,6 +229,50 @@ def test_mla_batch_beyond_one_scorer_launch():
     ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], sel_lists(sel_np, h["lens"]), wl.group,
                                   wl.scale, wl.head_dim_v, wl.v_is_k_prefix)
     check_attention(to_np(out), ref, float(torch.nan_to_num(x["k_pages"], 0.0).abs().max()), "mla many")
+
+
+@pytest.mark.parametrize("name", ["d128_g8", "mla", "d64_g4"])
+def test_forced_sink_and_recent_pages_match_oracle(name):
+    """Sink and recent pages kept beside the scored budget (appendix Tables
+    8-11): forced pages exact, the others by the gap rule, attention against
+    the oracle on the GPU's selection."""
+    wl, x = make(name)
+    summ = build_summaries(x, wl)
+    sink, recent, topk = 1, 2, max(wl.topk // 2, 1)
+    out, sel = run_sparse_decode(x, wl, summ, topk=topk, refresh=1, sink=sink, recent=recent)
+    h = host_inputs(x)
+    ref_summ = oracle.quest_summaries(h["k"], h["pt"], h["lens"])
+    A = oracle.quest_scores(h["q"], ref_summ, h["lens"], wl.group, wl.scale)
+    sel_np = to_np(sel)
+    for b, n in enumerate(h["lens"]):
+        Pb = -(-int(n) // 16)
+        for g in range(wl.num_kv_heads):
+            check_forced_selection(sel_np[b, g], A[b, g, :Pb], topk, sink, recent, f"{name} b{b} g{g}")
+    ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], sel_lists(sel_np, h["lens"]), wl.group,
+                                  wl.scale, wl.head_dim_v, wl.v_is_k_prefix)
+    vmax = float(torch.nan_to_num(x["v_pages"] if x["v_pages"] is not None else x["k_pages"], 0.0).abs().max())
+    check_attention(to_np(out), ref, vmax, f"{name} sink/recent")
+
+
+@pytest.mark.parametrize("name", ["d128_g8", "mla"])
+def test_sink_and_recent_only_needs_no_summaries(name):
+    """topk = 0 keeps exactly the sink and recent pages (the StreamingLLM rows of
+    appendix Tables 8-9), scores nothing and reads no summaries."""
+    wl, x = make(name)
+    sink, recent = 1, 3
+    out, sel = run_sparse_decode(x, wl, None, topk=0, refresh=0, sink=sink, recent=recent)
+    h = host_inputs(x)
+    sel_np = to_np(sel)
+    want = oracle.quest_select(np.zeros((wl.batch, wl.num_kv_heads, wl.max_pages)), h["lens"], 0, sink=sink,
+                               recent=recent)
+    for b in range(wl.batch):
+        for g in range(wl.num_kv_heads):
+            k = len(want[b][g])
+            assert (sel_np[b, g, :k] == want[b][g]).all() and (sel_np[b, g, k:] == -1).all(), f"b{b} g{g}"
+    ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], want, wl.group, wl.scale,
+                                  wl.head_dim_v, wl.v_is_k_prefix)
+    vmax = float(torch.nan_to_num(x["v_pages"] if x["v_pages"] is not None else x["k_pages"], 0.0).abs().max())
+    check_attention(to_np(out), ref, vmax, f"{name} sink/recent only")
 
 
 def test_empty_and_single_token_requests():

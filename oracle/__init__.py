@@ -33,6 +33,15 @@ Table 7):
       compaction by copying the kept rows (Table 15 note: physical eviction
       releases storage).
   O7  decode over the compacted cache: O5 with every kept row selected.
+  O8  the eviction family around O6's scores (appendix Tables 8-11): always
+      kept sink and recent tokens beside the selected budget (SnapKV rows
+      with a Sink and a Recent column; H2O's recent ratio with its 128-token
+      scoring window), a history interval outside which nothing is evicted
+      (Figure 4: prefix-cache pruning), and re-eviction of an already
+      compacted cache whose rows carry their original positions (Tables 9-10:
+      "eviction every 1,024 decode steps").
+  O9  PyramidKV's per-layer budgets: layer ratios falling linearly from the
+      first to the last layer (Tables 8-9, 11).
 
 Readings where the pages are silent are listed in the design notes; the ones
 that change numbers are noted next to the code that takes them.
@@ -348,22 +357,75 @@ def snapkv_unit_keep(pooled: np.ndarray, n: int, window: int, budget: int) -> np
     return np.concatenate([top, np.arange(L, n, dtype=np.int64)])
 
 
+def eviction_candidates(n: int, window: int, sink: int = 0, recent: int = 0, interval=None):
+    """O8: the range [lo, hi) of positions an eviction may drop; every
+    position outside it is kept.
+
+    The first ``sink`` positions are kept, and so are the last
+    max(recent, window) positions: the scoring window is always part of the
+    recent tokens (SnapKV keeps its window; appendix Tables 8-11 give each
+    method a Sink and a Recent budget beside the selected one, and H2O's
+    recent ratio reserves a share of its budget for the newest tokens).  With
+    a history interval [ib, ie) (Figure 4: the application names the span
+    that may be pruned) the range is further cut to it.  hi <= lo means there
+    is nothing to choose from.
+    """
+    lo = int(sink)
+    hi = int(n) - max(int(recent), int(window))
+    if interval is not None:
+        lo = max(lo, int(interval[0]))
+        hi = min(hi, int(interval[1]))
+    return lo, hi
+
+
+def eviction_unit_keep(pooled: np.ndarray, n: int, window: int, budget: int, sink: int = 0, recent: int = 0,
+                       interval=None) -> np.ndarray:
+    """O8: kept positions, ascending.  Everything outside the candidate range
+    [lo, hi) is kept; inside it the ``budget`` positions with the largest
+    pooled vote (ties to the lower position); when the range holds no more
+    than ``budget`` positions nothing is dropped.  ``pooled`` covers the
+    scored prefix [0, n - window).  With sink = recent = 0 and no interval
+    this is O6's selection (top budget of the prefix plus the window)."""
+    lo, hi = eviction_candidates(n, window, sink, recent, interval)
+    if hi - lo <= budget:
+        return np.arange(n, dtype=np.int64)
+    top = lo + unit_select(np.asarray(pooled)[lo:hi], budget)
+    return np.concatenate([np.arange(lo, dtype=np.int64), top, np.arange(hi, n, dtype=np.int64)])
+
+
+def eviction_kept_capacity(max_len: int, window: int, budget: int, sink: int = 0, recent: int = 0,
+                           interval=None) -> int:
+    """The most positions O8 can keep for any prompt length up to ``max_len``:
+    max(sink, ib) + budget + max(recent, window, max_len - ie).  A kept list
+    is at most this long whether or not anything is dropped."""
+    ib, ie = (0, int(max_len)) if interval is None else (int(interval[0]), int(interval[1]))
+    return max(int(sink), ib) + int(budget) + max(int(recent), int(window), int(max_len) - ie)
+
+
 def snapkv_compact(q_win, k, v, prompt_lens, group: int, scale: float, window: int, pool_kernel: int,
-                   budget: int, out_capacity: int):
-    """O6 for the whole batch.
+                   budget: int, out_capacity: int, sink: int = 0, recent: int = 0, interval=None,
+                   positions=None):
+    """O6 (with O8's forced positions and interval) for the whole batch.
 
     q_win bf16 bits [B, Hq, W, D]; k, v bf16 bits [B, Hkv, Nmax, D].
     Returns (k_out, v_out, kept_idx, kept_len, pooled) where k_out/v_out are
     bf16 bit arrays [B, Hkv, out_capacity, D] holding the kept rows (rows past
-    kept_len are zero), kept_idx is int [B, Hkv, budget+window] padded with
-    -1, and pooled[b][g] is the pooled vote vector (None when nothing is
-    scored).
+    kept_len are zero), kept_idx is int [B, Hkv, kcap] padded with -1 (kcap =
+    eviction_kept_capacity; budget + window without forced positions or an
+    interval), and pooled[b][g] is the pooled vote vector over the prefix
+    (None when nothing is scored).
+
+    ``positions`` (int [B, Hkv, Nmax], optional) re-evicts a cache that was
+    compacted before: row r of k/v holds the token at original position
+    positions[b][g][r], and kept_idx reports those original positions (the
+    rows copied are still the kept rows of k/v).  Nothing else changes: the
+    window is the last W rows of the cache and the softmax runs over its rows.
     """
     qf = bf16_to_f64(q_win)
     k = np.asarray(k)
     v = np.asarray(v)
-    B, Hkv, _, D = k.shape
-    cap = budget + window
+    B, Hkv, Nmax, D = k.shape
+    cap = eviction_kept_capacity(Nmax, window, budget, sink, recent, interval)
     k_out = np.zeros((B, Hkv, out_capacity, D), dtype=np.uint16)
     v_out = np.zeros((B, Hkv, out_capacity, D), dtype=np.uint16)
     kept_idx = np.full((B, Hkv, cap), -1, dtype=np.int64)
@@ -371,20 +433,54 @@ def snapkv_compact(q_win, k, v, prompt_lens, group: int, scale: float, window: i
     pooled = [[None] * Hkv for _ in range(B)]
     for b in range(B):
         n = int(prompt_lens[b])
+        lo, hi = eviction_candidates(n, window, sink, recent, interval)
         for g in range(Hkv):
-            if n - window <= budget:
+            if hi - lo <= budget:
                 keep = np.arange(n, dtype=np.int64)
             else:
                 keys = bf16_to_f64(k[b, g, :n])
                 S, _, _ = snapkv_unit_votes(qf[b, g * group:(g + 1) * group], keys, n, scale)
                 Sp = maxpool1d(S, pool_kernel)
                 pooled[b][g] = Sp
-                keep = snapkv_unit_keep(Sp, n, window, budget)
+                keep = eviction_unit_keep(Sp, n, window, budget, sink, recent, interval)
             kept_len[b, g] = len(keep)
-            kept_idx[b, g, :len(keep)] = keep
+            kept_idx[b, g, :len(keep)] = keep if positions is None else np.asarray(positions)[b, g, keep]
             k_out[b, g, :len(keep)] = k[b, g, keep]
             v_out[b, g, :len(keep)] = v[b, g, keep]
     return k_out, v_out, kept_idx, kept_len, pooled
+
+
+def pyramid_budgets(num_layers: int, budget: int, ratio_first: float, ratio_last: float):
+    """O9: PyramidKV's selected budget per layer.
+
+    The pages give layer ratios falling linearly from the first layer to the
+    last (Tables 8-9: 0.6 to 0.01; Table 11: 0.6 to 0.0154712 from layer 0)
+    beside one selected budget.  Reading: layer l's budget is proportional to
+    its ratio r_l = ratio_first + (ratio_last - ratio_first) * l / (L - 1),
+    and the layers share L * budget tokens in all, so the budgets average the
+    configured one.  The ratios are taken to nine decimals and the shares are
+    computed exactly (integers); the L * budget tokens are dealt as the
+    floors of the exact shares plus one more token to each of the layers with
+    the largest remainders, ties to the lower layer.
+    """
+    L = int(num_layers)
+    A = round(float(ratio_first) * 10**9)
+    Z = round(float(ratio_last) * 10**9)
+    if L == 1:
+        weights = [A]
+    else:
+        weights = [A * (L - 1) + (Z - A) * l for l in range(L)]  # r_l scaled by 1e9 * (L - 1)
+    total_w = sum(weights)
+    tokens = L * int(budget)
+    share = [tokens * w for w in weights]  # layer l's exact share is share[l] / total_w
+    floors = [s // total_w for s in share]
+    rems = [s % total_w for s in share]
+    extra = tokens - sum(floors)
+    order = sorted(range(L), key=lambda l: (-rems[l], l))
+    out = list(floors)
+    for l in order[:extra]:
+        out[l] += 1
+    return out
 
 
 def decode_over_rows(q, keys_bits, vals_bits, length: int, group: int, scale: float):

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 
 import oracle
+import test_oracle_eviction as te
 import test_oracle_quest as tq
 import test_oracle_snapkv as ts
 
@@ -43,6 +44,17 @@ def _pins():
         ts.test_identity_budget_keeps_everything_bitwise,
         ts.test_eviction_keeps_top_pooled_plus_window,
         ts.test_decode_over_compacted_cache,
+        te.test_worked_example_w3,
+        lambda: te.test_selection_against_pairwise_order.hypothesis.inner_test(
+            seed=13, n=40, W=3, R=6, sink=2, recent=7, use_iv=False, ib=0, span=1, levels=3),
+        lambda: te.test_selection_against_pairwise_order.hypothesis.inner_test(
+            seed=14, n=50, W=2, R=4, sink=0, recent=0, use_iv=True, ib=10, span=20, levels=50),
+        lambda: te.test_defaults_reduce_to_snapkv.hypothesis.inner_test(seed=15, n=30, W=3, R=5),
+        te.test_compact_with_forced_positions_and_interval,
+        te.test_reeviction_reports_original_positions,
+        te.test_pyramid_worked_examples,
+        lambda: te.test_pyramid_exact_shares.hypothesis.inner_test(L=47, R=4096, a=0.6, z=0.01),
+        te.test_pyramid_special_cases,
     ]
 
 
@@ -213,6 +225,63 @@ def decode_rows_one_short(q, keys_bits, vals_bits, length, group, scale):
                                   oracle.bf16_to_f64(np.asarray(vals_bits)[:, :length - 1]), group, scale)
 
 
+def candidates_recent_not_widened(n, window, sink=0, recent=0, interval=None):
+    lo, hi = int(sink), int(n) - int(recent)
+    if interval is not None:
+        lo, hi = max(lo, int(interval[0])), min(hi, int(interval[1]))
+    return lo, hi
+
+
+def candidates_sink_one_past(n, window, sink=0, recent=0, interval=None):
+    lo, hi = int(sink) + 1, int(n) - max(int(recent), int(window))
+    if interval is not None:
+        lo, hi = max(lo, int(interval[0])), min(hi, int(interval[1]))
+    return lo, hi
+
+
+def candidates_interval_end_inclusive(n, window, sink=0, recent=0, interval=None):
+    lo, hi = int(sink), int(n) - max(int(recent), int(window))
+    if interval is not None:
+        lo, hi = max(lo, int(interval[0])), min(hi, int(interval[1]) + 1)
+    return lo, hi
+
+
+_true_keep = oracle.eviction_unit_keep
+
+
+def keep_forced_inside_budget(pooled, n, window, budget, sink=0, recent=0, interval=None):
+    lo, hi = oracle.eviction_candidates(n, window, sink, recent, interval)
+    return _true_keep(pooled, n, window, max(budget - lo, 1), sink, recent, interval)
+
+
+def keep_candidates_from_zero(pooled, n, window, budget, sink=0, recent=0, interval=None):
+    lo, hi = oracle.eviction_candidates(n, window, sink, recent, interval)
+    if hi - lo <= budget:
+        return np.arange(n, dtype=np.int64)
+    top = oracle.unit_select(np.asarray(pooled)[lo:hi], budget)  # offset forgotten
+    return np.unique(np.concatenate([np.arange(lo), top, np.arange(hi, n)])).astype(np.int64)
+
+
+_true_pyramid = oracle.pyramid_budgets
+
+
+def pyramid_floors_only(num_layers, budget, ratio_first, ratio_last):
+    L = int(num_layers)
+    r = [ratio_first + (ratio_last - ratio_first) * l / max(L - 1, 1) for l in range(L)]
+    return [int(L * budget * x / sum(r)) for x in r]
+
+
+def pyramid_ratios_reversed(num_layers, budget, ratio_first, ratio_last):
+    return _true_pyramid(num_layers, budget, ratio_last, ratio_first)
+
+
+_true_compact = oracle.snapkv_compact
+
+
+def compact_positions_ignored(*args, positions=None, **kw):
+    return _true_compact(*args, **kw)
+
+
 MUTANTS = {
     "bound: min instead of max": ("unit_page_bounds", bound_min_instead_of_max),
     "bound: dropped min term": ("unit_page_bounds", bound_max_term_only),
@@ -240,6 +309,14 @@ MUTANTS = {
     "keep: window dropped": ("snapkv_unit_keep", keep_without_window),
     "keep: window shifted": ("snapkv_unit_keep", keep_window_shifted),
     "decode: one row short": ("decode_over_rows", decode_rows_one_short),
+    "evict: recent not widened to the window": ("eviction_candidates", candidates_recent_not_widened),
+    "evict: sink one past": ("eviction_candidates", candidates_sink_one_past),
+    "evict: interval end inclusive": ("eviction_candidates", candidates_interval_end_inclusive),
+    "evict: forced positions counted in the budget": ("eviction_unit_keep", keep_forced_inside_budget),
+    "evict: candidate offset forgotten": ("eviction_unit_keep", keep_candidates_from_zero),
+    "pyramid: floors only": ("pyramid_budgets", pyramid_floors_only),
+    "pyramid: ratios reversed": ("pyramid_budgets", pyramid_ratios_reversed),
+    "re-evict: positions ignored": ("snapkv_compact", compact_positions_ignored),
 }
 
 

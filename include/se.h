@@ -14,7 +14,13 @@
  *   kernel 7"): the last W queries score the context, the scores are summed
  *   and max-pooled, the top R prefix tokens plus the window are kept, and
  *   the kept K/V rows are copied into a dense retained cache, so storage is
- *   really released (Table 15 note).
+ *   really released (Table 15 note).  The same calls cover the eviction
+ *   methods the pages configure around those scores: sink and recent tokens
+ *   kept beside the selected budget (Tables 8-11), H2O (a 128-token scoring
+ *   window, no pooling, a recent share of the budget), PyramidKV (per-layer
+ *   budgets, se_pyramid_budgets), prefix-cache pruning inside a history
+ *   interval (Figure 4) and re-eviction during decode (Tables 9-10:
+ *   "eviction every 1,024 decode steps", se_snapkv_recompact).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -184,7 +190,7 @@ int se_decode_selected(const se_kv_layout* layout, const se_decode_params* param
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * SnapKV eviction and compaction.
+ * SnapKV eviction and compaction, and the eviction family around it.
  *
  * Per request b (prompt length n = prompt_lens[b]) and KV head g, with
  * L = n - window:
@@ -195,10 +201,24 @@ int se_decode_selected(const se_kv_layout* layout, const se_decode_params* param
  *     probabilities, for prefix positions j < L;
  *   - pooled votes = stride-1 centred max-pool of odd width pool_kernel,
  *     cut at both ends of the prefix;
- *   - kept = the `budget` prefix positions with the largest pooled vote
- *     (ties to the lower position) plus the window positions L..n-1, in
- *     ascending order; when L <= budget every position 0..n-1 is kept;
+ *   - candidates [lo, hi): lo = max(sink, interval_begin),
+ *     hi = min(n - max(recent, window), interval_end) (interval_end = n when
+ *     no interval is given); every position outside them is kept;
+ *   - kept = 0..lo-1, the `budget` candidates with the largest pooled vote
+ *     (ties to the lower position), and hi..n-1, in ascending order; when
+ *     hi - lo <= budget every position 0..n-1 is kept.  With sink = recent
+ *     = 0 and no interval this is SnapKV's top-R prefix plus the window;
  *   - k_out[b][g][r] = k[b][g][kept[r]] and likewise v_out (bit copies).
+ *
+ * The methods of the pages' tables as settings of these fields:
+ *   SnapKV (Table 8)     window 32, pool 7, budget 2016, recent 32
+ *   SnapKV (Table 9)     window 16, pool 7, budget 4096, sink 16, recent 64
+ *   H2O (Table 8)        window 128, pool 1, total T = 8192 split by the
+ *                        recent ratio 0.5: recent = 4096, budget = 4096
+ *   PyramidKV (Table 8)  window 32, sink 64, recent 512, budget per layer
+ *                        from se_pyramid_budgets(L, 4096, 0.6, 0.01)
+ *   prefix-cache pruning an interval [ib, ie) naming the history span that
+ *   (Figure 4)           may be pruned; everything outside it is kept
  * ------------------------------------------------------------------------- */
 typedef struct se_snapkv_params {
   int32_t batch;           /* B                                              */
@@ -206,31 +226,77 @@ typedef struct se_snapkv_params {
   int32_t num_kv_heads;    /* Hkv                                            */
   int32_t head_dim;        /* D; 128 or 64                                   */
   int32_t max_prompt_len;  /* token dim of k, v: [B, Hkv, max_prompt_len, D] */
-  int32_t window;          /* W, 1..64                                        */
+  int32_t window;          /* W, 1..128                                       */
   int32_t pool_kernel;     /* odd, 1 .. 129 (wider: SE_EUNSUPPORTED)          */
-  int32_t budget;          /* R >= 1 prefix tokens kept                       */
-  int32_t out_capacity;    /* token dim of k_out/v_out, >= budget + window    */
+  int32_t budget;          /* R >= 1 candidates kept                          */
+  int32_t out_capacity;    /* token dim of k_out/v_out, >= the kept capacity  */
   float sm_scale;          /* s; 0 means 1/sqrt(D)                            */
+  int32_t sink;            /* >= 0 leading positions always kept              */
+  int32_t recent;          /* >= 0 trailing positions always kept (at least
+                              the window is)                                 */
+  int32_t interval_begin;  /* history interval [begin, end) that may be      */
+  int32_t interval_end;    /* pruned, 0 <= begin < end <= max_prompt_len;
+                              both 0: no interval                            */
 } se_snapkv_params;
+
+/* Row length kcap of kept_idx: the most positions a request of any length up
+ * to max_prompt_len keeps, max(sink, interval_begin) + budget +
+ * max(recent, window, max_prompt_len - interval_end); budget + window for
+ * plain SnapKV.  out_capacity must be at least kcap. */
+int se_snapkv_kept_capacity(const se_snapkv_params* params, int32_t* kcap);
 
 int se_snapkv_workspace_size(const se_snapkv_params* params, size_t* bytes);
 
 /*   q_win       bf16 [B, Hq, W, D]   queries of the last W prompt positions
  *   k, v        bf16 [B, Hkv, max_prompt_len, D]
  *   prompt_lens int32 [B], each in [1, max_prompt_len]
- *   k_out,v_out bf16 [B, Hkv, out_capacity, D]; rows past kept_len untouched
- *   kept_idx    int32 [B, Hkv, budget + W], ascending, -1 padded
+ *   k_out,v_out bf16 [B, Hkv, out_capacity, D]; rows past kept_len untouched;
+ *               must not overlap k or v (SE_EINVAL)
+ *   kept_idx    int32 [B, Hkv, kcap], ascending, -1 padded
  *   kept_len    int32 [B, Hkv]
  * After the call completes the caller may release k and v. */
 int se_snapkv_compact(const se_snapkv_params* params, const void* q_win, const void* k, const void* v,
                       const int32_t* prompt_lens, void* k_out, void* v_out, int32_t* kept_idx,
                       int32_t* kept_len, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Re-eviction of a cache that was compacted before (SparseEngine Tables 9-10:
+ * SnapKV, H2O and PyramidKV evict again every 1,024 decode steps).  k, v are
+ * the retained cache [B, Hkv, max_prompt_len, D] with the decode steps'
+ * rows appended; cache_lens[b] counts its rows (kept prompt rows plus decode
+ * steps); q_win holds the queries of the last W decode steps.  Everything is
+ * computed as in se_snapkv_compact over the rows of the cache, except that
+ * kept_idx receives original positions: positions int32 [B, Hkv,
+ * max_prompt_len] gives the position row r of (b, g) stands for (the
+ * previous kept_idx, followed by the decode steps' positions).  positions
+ * must be non-NULL when batch > 0 (SE_EINVAL); k_out/v_out must not overlap
+ * k/v (the caller double-buffers). */
+int se_snapkv_recompact(const se_snapkv_params* params, const void* q_win, const void* k, const void* v,
+                        const int32_t* cache_lens, const int32_t* positions, void* k_out, void* v_out,
+                        int32_t* kept_idx, int32_t* kept_len, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* PyramidKV's selected budget per layer (SparseEngine Tables 8-9: "layer
+ * ratios 0.6 to 0.01 (linear)"; Table 11: 0.6 to 0.0154712 from layer 0).
+ * HOST function, no GPU work: budgets is a HOST array [num_layers].  Layer
+ * l's budget is proportional to r_l = ratio_first + (ratio_last -
+ * ratio_first) * l / (num_layers - 1); the layers share num_layers * budget
+ * tokens, dealt as the floors of the exact shares plus one token each to
+ * the layers with the largest remainders (ties to the lower layer).  Ratios
+ * are taken to nine decimals (rounded half to even) and the shares are exact
+ * integer arithmetic.  Errors: SE_EINVAL for a NULL array, num_layers < 1,
+ * budget < 1 or a ratio outside (0, 1000]; SE_EUNSUPPORTED for more than
+ * 4096 layers or a budget above 2^24.  A layer's budget can be 0 for a
+ * vanishing ratio; callers evict with budget >= 1. */
+int se_pyramid_budgets(int32_t num_layers, int32_t budget, double ratio_first, double ratio_last,
+                       int32_t* budgets);
+
 /* The steps of se_snapkv_compact, exposed one by one.
  * votes/pooled: fp32 [B, Hkv, max_prompt_len]; entries j < L are written for
  * every request with n > W (se_snapkv_votes) and n - W > budget is not
  * required; other entries are untouched.  se_snapkv_votes needs the same
- * workspace as se_snapkv_compact. */
+ * workspace as se_snapkv_compact.  se_maxpool1d pools the whole prefix;
+ * se_snapkv_select writes kept_idx [B, Hkv, kcap] of prompt positions and
+ * se_compact copies the rows kept_idx names. */
 int se_snapkv_votes(const se_snapkv_params* params, const void* q_win, const void* k,
                     const int32_t* prompt_lens, float* votes, void* workspace, size_t workspace_bytes,
                     void* stream);

@@ -51,7 +51,9 @@ class SnapKVParams(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("max_prompt_len", ctypes.c_int32), ("window", ctypes.c_int32),
                 ("pool_kernel", ctypes.c_int32), ("budget", ctypes.c_int32),
-                ("out_capacity", ctypes.c_int32), ("sm_scale", ctypes.c_float)]
+                ("out_capacity", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+                ("sink", ctypes.c_int32), ("recent", ctypes.c_int32),
+                ("interval_begin", ctypes.c_int32), ("interval_end", ctypes.c_int32)]
 
 
 _lib = None
@@ -72,6 +74,10 @@ _SIG = {
     "se_maxpool1d": ([_P, _P, _P, _P, _P], ctypes.c_int),
     "se_snapkv_select": ([_P, _P, _P, _P, _P, _P], ctypes.c_int),
     "se_compact": ([_P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
+    "se_snapkv_kept_capacity": ([_P, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
+    "se_snapkv_recompact": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "se_pyramid_budgets": ([_I, _I, ctypes.c_double, ctypes.c_double, ctypes.POINTER(ctypes.c_int32)],
+                           ctypes.c_int),
 }
 
 
@@ -150,9 +156,9 @@ def kept_capacity(params: DecodeParams) -> int:
 
 
 def snapkv_params(batch, num_q_heads, num_kv_heads, head_dim, max_prompt_len, window, pool_kernel, budget,
-                  out_capacity, sm_scale=0.0) -> SnapKVParams:
+                  out_capacity, sm_scale=0.0, sink=0, recent=0, interval=(0, 0)) -> SnapKVParams:
     return SnapKVParams(batch, num_q_heads, num_kv_heads, head_dim, max_prompt_len, window, pool_kernel, budget,
-                        out_capacity, sm_scale)
+                        out_capacity, sm_scale, sink, recent, interval[0], interval[1])
 
 
 # ---------------------------------------------------------------------------
@@ -212,6 +218,27 @@ def se_snapkv_compact(params, q_win, k, v, prompt_lens, k_out, v_out, kept_idx, 
     _check(lib().se_snapkv_compact(ctypes.byref(params), _ptr(q_win), _ptr(k), _ptr(v), _ptr(prompt_lens),
                                    _ptr(k_out), _ptr(v_out), _ptr(kept_idx), _ptr(kept_len), _ptr(workspace),
                                    _nbytes(workspace), _stream(stream)), "se_snapkv_compact")
+
+
+def se_snapkv_kept_capacity(params) -> int:
+    n = ctypes.c_int32(0)
+    _check(lib().se_snapkv_kept_capacity(ctypes.byref(params), ctypes.byref(n)), "se_snapkv_kept_capacity")
+    return n.value
+
+
+def se_snapkv_recompact(params, q_win, k, v, cache_lens, positions, k_out, v_out, kept_idx, kept_len, workspace,
+                        stream=None):
+    _check(lib().se_snapkv_recompact(ctypes.byref(params), _ptr(q_win), _ptr(k), _ptr(v), _ptr(cache_lens),
+                                     _ptr(positions), _ptr(k_out), _ptr(v_out), _ptr(kept_idx), _ptr(kept_len),
+                                     _ptr(workspace), _nbytes(workspace), _stream(stream)), "se_snapkv_recompact")
+
+
+def se_pyramid_budgets(num_layers, budget, ratio_first, ratio_last) -> list:
+    """Host-side arithmetic in the library; returns a list of num_layers ints."""
+    out = (ctypes.c_int32 * max(int(num_layers), 1))()
+    _check(lib().se_pyramid_budgets(int(num_layers), int(budget), float(ratio_first), float(ratio_last), out),
+           "se_pyramid_budgets")
+    return list(out)[:int(num_layers)]
 
 
 def se_snapkv_votes(params, q_win, k, prompt_lens, votes, workspace, stream=None):

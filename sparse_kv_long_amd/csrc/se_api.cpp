@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <new>
+
 #include "../../include/se.h"
 #include "se_internal.h"
 
@@ -12,7 +14,7 @@ namespace {
 
 using se::Layout;
 
-constexpr int kVersion = 200;  // 0.2.0: forced sink and recent pages
+constexpr int kVersion = 300;  // 0.3.0: eviction family (sink/recent, interval, re-eviction), layer budgets
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -98,6 +100,16 @@ DecodeWs decode_ws(const se_kv_layout* L, const se_decode_params* p, bool dense)
 
 int hip_status(hipError_t e) { return e == hipSuccess ? SE_OK : SE_EHIP; }
 
+// Row length of kept_idx: the most positions any prompt length up to
+// max_prompt_len can keep, max(sink, ib) + budget + max(recent, window, N - ie).
+int64_t snap_kept_capacity(const se_snapkv_params* p) {
+  const bool iv = p->interval_end != 0;
+  const int64_t ib = iv ? p->interval_begin : 0, ie = iv ? p->interval_end : p->max_prompt_len;
+  int64_t tail = p->recent > p->window ? p->recent : p->window;
+  if (p->max_prompt_len - ie > tail) tail = p->max_prompt_len - ie;
+  return (p->sink > ib ? p->sink : ib) + (int64_t)p->budget + tail;
+}
+
 int check_snap(const se_snapkv_params* p) {
   if (!p) return SE_EINVAL;
   if (p->batch < 0 || p->num_kv_heads < 1 || p->num_q_heads < 1 || p->max_prompt_len < 1) return SE_EINVAL;
@@ -105,11 +117,17 @@ int check_snap(const se_snapkv_params* p) {
   if (p->num_q_heads / p->num_kv_heads > 32) return SE_EUNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return SE_EUNSUPPORTED;
   if (p->window < 1 || p->budget < 1) return SE_EINVAL;
-  if (p->window > 64) return SE_EUNSUPPORTED;
+  if (p->window > 128) return SE_EUNSUPPORTED;
   if (p->pool_kernel < 1 || p->pool_kernel % 2 == 0) return SE_EINVAL;
   if (p->pool_kernel > se::kMaxPoolKernel) return SE_EUNSUPPORTED;
-  if (p->out_capacity < p->budget + p->window) return SE_EINVAL;
+  if (p->sink < 0 || p->recent < 0) return SE_EINVAL;
+  if (p->interval_end != 0 &&
+      (p->interval_begin < 0 || p->interval_begin >= p->interval_end || p->interval_end > p->max_prompt_len))
+    return SE_EINVAL;
+  if (p->interval_end == 0 && p->interval_begin != 0) return SE_EINVAL;
   if (p->max_prompt_len - p->window > 65536) return SE_EUNSUPPORTED;
+  if (snap_kept_capacity(p) > INT32_MAX / 2) return SE_EINVAL;
+  if (p->out_capacity < snap_kept_capacity(p)) return SE_EINVAL;
   if (!(p->sm_scale >= 0.f) || isinf(p->sm_scale)) return SE_EINVAL;
   return SE_OK;
 }
@@ -130,6 +148,11 @@ se::SnapArgs snap_args(const se_snapkv_params* p, const void* q_win, const void*
   a.pool = p->pool_kernel;
   a.R = p->budget;
   a.cap = p->out_capacity;
+  a.sink = p->sink;
+  a.rec = p->recent > p->window ? p->recent : p->window;
+  a.ib = p->interval_end != 0 ? p->interval_begin : 0;
+  a.ie = p->interval_end != 0 ? p->interval_end : p->max_prompt_len;
+  a.kcap = (int)snap_kept_capacity(p);
   a.scale = p->sm_scale > 0.f ? p->sm_scale : 1.f / sqrtf((float)p->head_dim);
   return a;
 }
@@ -341,14 +364,34 @@ static int check_ws(const se::SnapArgs& a, void* ws, size_t bytes) {
   return SE_OK;
 }
 
-int se_snapkv_compact(const se_snapkv_params* params, const void* q_win, const void* k, const void* v,
-                      const int32_t* prompt_lens, void* k_out, void* v_out, int32_t* kept_idx, int32_t* kept_len,
-                      void* workspace, size_t workspace_bytes, void* stream) {
+int se_snapkv_kept_capacity(const se_snapkv_params* params, int32_t* kcap) {
+  const int rc = check_snap(params);
+  if (rc) return rc;
+  if (!kcap) return SE_EINVAL;
+  *kcap = (int32_t)snap_kept_capacity(params);
+  return SE_OK;
+}
+
+// [a, a + na) and [b, b + nb) share a byte
+static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return x < y + nb && y < x + na;
+}
+
+static int snap_evict(const se_snapkv_params* params, const void* q_win, const void* k, const void* v,
+                      const int32_t* prompt_lens, const int32_t* positions, void* k_out, void* v_out,
+                      int32_t* kept_idx, int32_t* kept_len, void* workspace, size_t workspace_bytes, void* stream) {
   int rc = check_snap(params);
   if (rc) return rc;
   if (params->batch == 0) return SE_OK;
   if (!q_win || !k || !v || !prompt_lens || !k_out || !v_out || !kept_idx || !kept_len) return SE_EINVAL;
   if (!aligned16(q_win) || !aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out)) return SE_EINVAL;
+  // the compaction reads rows of k/v while it writes k_out/v_out
+  const size_t in_bytes = (size_t)params->batch * params->num_kv_heads * params->max_prompt_len * params->head_dim * 2;
+  const size_t out_bytes = (size_t)params->batch * params->num_kv_heads * params->out_capacity * params->head_dim * 2;
+  if (overlaps(k, in_bytes, k_out, out_bytes) || overlaps(k, in_bytes, v_out, out_bytes) ||
+      overlaps(v, in_bytes, k_out, out_bytes) || overlaps(v, in_bytes, v_out, out_bytes))
+    return SE_EINVAL;
   const se::SnapArgs a = snap_args(params, q_win, k, v, prompt_lens);
   rc = check_ws(a, workspace, workspace_bytes);
   if (rc) return rc;
@@ -360,8 +403,61 @@ int se_snapkv_compact(const se_snapkv_params* params, const void* q_win, const v
   if (rc) return rc;
   rc = hip_status(se::launch_snap_select(a, w.pooled, kept_idx, kept_len, st));
   if (rc) return rc;
-  return hip_status(se::launch_compact(a, kept_idx, kept_len, static_cast<uint16_t*>(k_out),
-                                       static_cast<uint16_t*>(v_out), st));
+  rc = hip_status(se::launch_compact(a, kept_idx, kept_len, static_cast<uint16_t*>(k_out),
+                                     static_cast<uint16_t*>(v_out), st));
+  if (rc || !positions) return rc;
+  return hip_status(se::launch_map_positions(a, positions, kept_idx, kept_len, st));
+}
+
+int se_snapkv_compact(const se_snapkv_params* params, const void* q_win, const void* k, const void* v,
+                      const int32_t* prompt_lens, void* k_out, void* v_out, int32_t* kept_idx, int32_t* kept_len,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  return snap_evict(params, q_win, k, v, prompt_lens, nullptr, k_out, v_out, kept_idx, kept_len, workspace,
+                    workspace_bytes, stream);
+}
+
+int se_snapkv_recompact(const se_snapkv_params* params, const void* q_win, const void* k, const void* v,
+                        const int32_t* cache_lens, const int32_t* positions, void* k_out, void* v_out,
+                        int32_t* kept_idx, int32_t* kept_len, void* workspace, size_t workspace_bytes, void* stream) {
+  if (params && params->batch > 0 && !positions) return SE_EINVAL;
+  return snap_evict(params, q_win, k, v, cache_lens, positions, k_out, v_out, kept_idx, kept_len, workspace,
+                    workspace_bytes, stream);
+}
+
+int se_pyramid_budgets(int32_t num_layers, int32_t budget, double ratio_first, double ratio_last,
+                       int32_t* budgets) {
+  if (!budgets || num_layers < 1 || budget < 1) return SE_EINVAL;
+  if (num_layers > 4096 || budget > (1 << 24)) return SE_EUNSUPPORTED;
+  if (!(ratio_first > 0.0 && ratio_first <= 1000.0) || !(ratio_last > 0.0 && ratio_last <= 1000.0))
+    return SE_EINVAL;
+  // ratios to nine decimals (round half to even), then exact integer shares
+  const int64_t A = (int64_t)nearbyint(ratio_first * 1e9), Z = (int64_t)nearbyint(ratio_last * 1e9);
+  if (A < 1 || Z < 1) return SE_EINVAL;
+  const int L = num_layers;
+  __int128 total_w = 0;
+  for (int l = 0; l < L; ++l) total_w += L == 1 ? A : (__int128)A * (L - 1) + (__int128)(Z - A) * l;
+  const __int128 tokens = (__int128)L * budget;
+  __int128 given = 0;
+  // floors of the exact shares; remainders kept for the leftover tokens
+  __int128* rem = new (std::nothrow) __int128[L];
+  if (!rem) return SE_EINVAL;
+  for (int l = 0; l < L; ++l) {
+    const __int128 w = L == 1 ? A : (__int128)A * (L - 1) + (__int128)(Z - A) * l;
+    const __int128 share = tokens * w;
+    budgets[l] = (int32_t)(share / total_w);
+    rem[l] = share % total_w;
+    given += budgets[l];
+  }
+  // one more token to each of the layers with the largest remainders, ties to the lower layer
+  for (__int128 extra = tokens - given; extra > 0; --extra) {
+    int best = -1;
+    for (int l = 0; l < L; ++l)
+      if (rem[l] >= 0 && (best < 0 || rem[l] > rem[best])) best = l;
+    budgets[best] += 1;
+    rem[best] = -1;
+  }
+  delete[] rem;
+  return SE_OK;
 }
 
 int se_snapkv_votes(const se_snapkv_params* params, const void* q_win, const void* k, const int32_t* prompt_lens,

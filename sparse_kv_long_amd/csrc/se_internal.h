@@ -63,8 +63,20 @@ struct SnapArgs {
   const uint16_t* v;
   const int32_t* lens;
   int B, Hq, Hkv, D, N, W, pool, R, cap;
+  int sink;  // leading positions always kept
+  int rec;   // trailing positions always kept: max(recent, W)
+  int ib;    // history interval [ib, ie) outside which nothing is dropped (0, N without one)
+  int ie;
+  int kcap;  // row length of kept_idx: max(sink, ib) + R + max(rec, N - ie)
   float scale;
 };
+
+// Positions a request of length n may drop: [lo, hi); hi - lo <= R means
+// nothing is dropped (every position is kept).
+__host__ __device__ inline void snap_candidates(const SnapArgs& a, int n, int& lo, int& hi) {
+  lo = a.sink > a.ib ? a.sink : a.ib;
+  hi = n - a.rec < a.ie ? n - a.rec : a.ie;
+}
 struct SnapWork {
   float* row_part;  // [B, Hkv, row_groups, nblk*waves, 128, 2] partial (max, sum)
   float* row_c;     // [B, Hq, W]   log2-domain normaliser per window row
@@ -83,5 +95,8 @@ hipError_t launch_snap_select(const SnapArgs& a, const float* pooled, int32_t* k
                               hipStream_t st);
 hipError_t launch_compact(const SnapArgs& a, const int32_t* kept_idx, const int32_t* kept_len, uint16_t* k_out,
                           uint16_t* v_out, hipStream_t st);
+// kept_idx[b][g][r] = positions[b][g][kept_idx[b][g][r]] for r < kept_len[b][g]
+hipError_t launch_map_positions(const SnapArgs& a, const int32_t* positions, int32_t* kept_idx,
+                                const int32_t* kept_len, hipStream_t st);
 
 }  // namespace se

@@ -42,6 +42,24 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const
 // (M index) 8*(r/4) + 4*(lane/32) + r%4, column (N index) lane%32.
 __device__ __forceinline__ int mfma_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// True when request length n leaves no more candidates than the budget, so
+// every position is kept and nothing needs scoring.
+__device__ __forceinline__ bool nothing_dropped(const SnapArgs& a, int n) {
+  int lo, hi;
+  snap_candidates(a, n, lo, hi);
+  return hi - lo <= a.R;
+}
+
+// Prefix columns [vlo, vhi) whose votes the selection reads: its candidates
+// [lo, hi) widened by the pooling radius, cut to the prefix [0, n - W).
+__device__ __forceinline__ void vote_span(const SnapArgs& a, int n, int& vlo, int& vhi) {
+  int lo, hi;
+  snap_candidates(a, n, lo, hi);
+  const int r = a.pool / 2;
+  vlo = max(lo - r, 0);
+  vhi = min(hi + r, n - a.W);
+}
+
 struct SnapGeom {
   int rows;   // G*W
   int nrg;    // row groups of up to 128 rows
@@ -131,7 +149,7 @@ __global__ __launch_bounds__(256) void snap_rowstats_kernel(SnapArgs a, float* _
   const int b = blockIdx.z, g = blockIdx.y / nrg, rg = blockIdx.y % nrg;
   const int n = a.lens[b];
   const int L = n - a.W;
-  if (L <= 0 || (skip_kept && L <= a.R)) return;
+  if (L <= 0 || (skip_kept && nothing_dropped(a, n))) return;
   const int G = a.Hq / a.Hkv;
   const int rows = G * a.W;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -208,7 +226,7 @@ __global__ __launch_bounds__(128) void snap_rowmerge_kernel(SnapArgs a, const fl
   const int b = blockIdx.y, g = blockIdx.x;
   const int n = a.lens[b];
   const int L = n - a.W;
-  if (L <= 0 || (skip_kept && L <= a.R)) return;
+  if (L <= 0 || (skip_kept && nothing_dropped(a, n))) return;
   const int G = a.Hq / a.Hkv;
   const int rows = G * a.W;
   for (int r = threadIdx.x; r < rows; r += blockDim.x) {
@@ -240,11 +258,15 @@ __global__ __launch_bounds__(256) void snap_votes_kernel(SnapArgs a, const float
   const int b = blockIdx.z, g = blockIdx.y / nrg, rg = blockIdx.y % nrg;
   const int n = a.lens[b];
   const int L = n - a.W;
-  if (L <= 0 || (skip_kept && L <= a.R)) return;
+  if (L <= 0 || (skip_kept && nothing_dropped(a, n))) return;
   const int G = a.Hq / a.Hkv;
   const int rows = G * a.W;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int slot = blockIdx.x * kSnapWaves + wave;
+  // columns whose votes are needed: the whole prefix, or (when selecting)
+  // the candidates plus the pooling halo
+  int vlo = 0, vhi = L;
+  if (skip_kept) vote_span(a, n, vlo, vhi);
   for (int r = threadIdx.x; r < kRowsPerGroup; r += blockDim.x) {
     const int gr = rg * kRowsPerGroup + r;
     // rows past G*W get +inf so their weight 2^(z - c) is 0
@@ -256,11 +278,12 @@ __global__ __launch_bounds__(256) void snap_votes_kernel(SnapArgs a, const float
   load_q_frags<D, NRT>(a, b, g, rg, rows, qf);
   const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + g) * a.N * D;
   float* vrow = votes + (((int64_t)rg * a.B + b) * a.Hkv + g) * a.N;
-  const int tiles = (L + 31) / 32;
+  const int t0 = vlo / 32;
+  const int tiles = (vhi + 31) / 32 - t0;
   // the slot's tiles in descending order: pass 1 read them ascending, so the
   // ones it read last (the likeliest still in the caches) come first
-  const int kt_last = slot < tiles ? slot + (tiles - 1 - slot) / slots * slots : -1;
-  for (int kt = kt_last; kt >= 0; kt -= slots) {
+  const int kt_last = slot < tiles ? t0 + slot + (tiles - 1 - slot) / slots * slots : -1;
+  for (int kt = kt_last; kt >= t0; kt -= slots) {
     uint4 kf[D / 16];
     load_k_frags<D>(kbase, kt, n, kf);
     float vote = 0.f;
@@ -324,20 +347,28 @@ hipError_t launch_snap_votes(const SnapArgs& a, const SnapWork& w, bool skip_kep
 constexpr int kPoolTile = 256;
 constexpr int kPoolMaxRadius = kMaxPoolKernel / 2;
 
-__global__ __launch_bounds__(kPoolTile) void maxpool_kernel(const float* __restrict__ votes,
-                                                            const int32_t* __restrict__ lens,
-                                                            float* __restrict__ pooled, int B, int Hkv, int N, int W,
-                                                            int R, int radius, int nrg, int skip_kept) {
+__global__ __launch_bounds__(kPoolTile) void maxpool_kernel(SnapArgs a, const float* __restrict__ votes,
+                                                            float* __restrict__ pooled, int radius, int nrg,
+                                                            int skip_kept) {
   __shared__ float sv[kPoolTile + 2 * kPoolMaxRadius];
   const int j0 = blockIdx.x * kPoolTile;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int L = lens[b] - W;
-  if (j0 >= L || (skip_kept && L <= R)) return;
-  const int span = min(kPoolTile + 2 * radius, L - (j0 - radius));
+  const int B = a.B, Hkv = a.Hkv, N = a.N;
+  const int n = a.lens[b];
+  const int L = n - a.W;
+  // positions pooled: the whole prefix, or (when selecting) the candidates,
+  // whose windows read only the columns the votes pass wrote
+  int lo = 0, hi = L, vlo = 0, vhi = L;
+  if (skip_kept) {
+    if (nothing_dropped(a, n)) return;
+    snap_candidates(a, n, lo, hi);
+    vote_span(a, n, vlo, vhi);
+  }
+  if (j0 >= hi || j0 + kPoolTile <= lo) return;
   for (int i = threadIdx.x; i < kPoolTile + 2 * radius; i += kPoolTile) {
     const int t = j0 - radius + i;
     float v = -__builtin_inff();
-    if (t >= 0 && t < L && i < span) {
+    if (t >= vlo && t < vhi) {
       v = 0.f;
       for (int rg = 0; rg < nrg; ++rg) v += votes[(((int64_t)rg * B + b) * Hkv + g) * N + t];
     }
@@ -345,7 +376,7 @@ __global__ __launch_bounds__(kPoolTile) void maxpool_kernel(const float* __restr
   }
   __syncthreads();
   const int j = j0 + threadIdx.x;
-  if (j >= L) return;
+  if (j < lo || j >= hi) return;
   float best = -__builtin_inff();
   for (int d = 0; d <= 2 * radius; ++d) best = fmaxf(best, sv[threadIdx.x + d]);
   pooled[((int64_t)b * Hkv + g) * N + j] = best;
@@ -356,8 +387,8 @@ hipError_t launch_maxpool(const SnapArgs& a, const float* votes, int row_groups,
   if (a.B == 0) return hipSuccess;
   if (a.pool / 2 > kPoolMaxRadius) return hipErrorInvalidValue;
   dim3 grid((a.N + kPoolTile - 1) / kPoolTile, a.Hkv, a.B);
-  hipLaunchKernelGGL(maxpool_kernel, grid, dim3(kPoolTile), 0, st, votes, a.lens, pooled, a.B, a.Hkv, a.N, a.W, a.R,
-                     a.pool / 2, row_groups, skip_kept ? 1 : 0);
+  hipLaunchKernelGGL(maxpool_kernel, grid, dim3(kPoolTile), 0, st, a, votes, pooled, a.pool / 2, row_groups,
+                     skip_kept ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -386,11 +417,36 @@ __global__ __launch_bounds__(256) void compact_kernel(const uint16_t* __restrict
 hipError_t launch_compact(const SnapArgs& a, const int32_t* kept_idx, const int32_t* kept_len, uint16_t* k_out,
                           uint16_t* v_out, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
-  const int cap_idx = a.R + a.W;
+  const int cap_idx = a.kcap;
   const int64_t chunks = (int64_t)cap_idx * (a.D / 8);
   dim3 grid((unsigned)((chunks + 255) / 256), a.Hkv, a.B);
   hipLaunchKernelGGL(compact_kernel, grid, dim3(256), 0, st, a.k, a.v, kept_idx, kept_len, k_out, v_out, a.Hkv, a.N,
                      a.D, cap_idx, a.cap);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Re-eviction of a compacted cache: the kept rows' indices become the
+// original positions those rows stand for.  One thread per kept row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void map_positions_kernel(const int32_t* __restrict__ positions,
+                                                            int32_t* __restrict__ kept_idx,
+                                                            const int32_t* __restrict__ kept_len, int Hkv, int N,
+                                                            int kcap) {
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int64_t bg = (int64_t)b * Hkv + g;
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= kept_len[bg]) return;
+  const int row = kept_idx[bg * kcap + r];
+  kept_idx[bg * kcap + r] = positions[bg * N + row];
+}
+
+hipError_t launch_map_positions(const SnapArgs& a, const int32_t* positions, int32_t* kept_idx,
+                                const int32_t* kept_len, hipStream_t st) {
+  if (a.B == 0) return hipSuccess;
+  dim3 grid((unsigned)((a.kcap + 255) / 256), a.Hkv, a.B);
+  hipLaunchKernelGGL(map_positions_kernel, grid, dim3(256), 0, st, positions, kept_idx, kept_len, a.Hkv, a.N,
+                     a.kcap);
   return hipGetLastError();
 }
 

@@ -94,15 +94,15 @@ __device__ __forceinline__ void block_and_or(uint32_t& vand, uint32_t& vor, Topk
   }
 }
 
-// Requires 0 < k < N <= KPT * 1024.  Writes k indices into out[0..k) and,
-// when `translate` is given, translate[index] into out2[0..k).  Indices below
-// `forced_lo` or from `forced_hi` on take the largest key, so they are always
-// kept (their number must not exceed k).
+// Requires 0 < k < N <= KPT * 1024.  Writes k indices (plus idx_base) into
+// out[0..k) and, when `translate` is given, translate[index] into out2[0..k).
+// Indices below `forced_lo` or from `forced_hi` on take the largest key, so
+// they are always kept (their number must not exceed k).
 template <int KPT>
 __device__ __forceinline__ void block_topk(const float* __restrict__ row, int N, int k, int32_t* __restrict__ out,
                                            TopkShared& sm,
                            const int32_t* __restrict__ translate = nullptr, int32_t* __restrict__ out2 = nullptr,
-                           int forced_lo = 0, int forced_hi = 0x7fffffff) {
+                           int forced_lo = 0, int forced_hi = 0x7fffffff, int idx_base = 0) {
   const int tid = threadIdx.x;
   const int base = tid * KPT;
   uint32_t key[KPT];
@@ -235,7 +235,7 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ row, int N,
       }
       if (sel) {
         if (out2) out2[pos] = tr[i];
-        out[pos++] = base + i;
+        out[pos++] = idx_base + base + i;
       }
     }
   }
@@ -312,30 +312,35 @@ hipError_t launch_topk_pages(int B, int Hkv, int MP, int topk, int sink, int rec
 }
 
 // ---------------------------------------------------------------------------
-// SnapKV: prefix tokens of (b, g) by pooled vote.  L = n - W; if L <= R keep
-// 0..n-1; else keep top-R of pooled[0..L) then L..n-1.  Output kept_idx
-// [B, Hkv, R+W] ascending and -1 padded; kept_len [B, Hkv].
+// SnapKV and its family: positions of (b, g) by pooled vote.  With [lo, hi)
+// the candidates (snap_candidates): if hi - lo <= R keep 0..n-1; else keep
+// 0..lo-1, the top R of pooled[lo..hi) (ties to the lower position), and
+// hi..n-1.  Output kept_idx [B, Hkv, kcap] ascending and -1 padded;
+// kept_len [B, Hkv].
 // ---------------------------------------------------------------------------
 template <int KPT>
-__global__ __launch_bounds__(kTopkThreads) void snap_select_kernel(const float* __restrict__ pooled,
-                                                                   const int32_t* __restrict__ lens,
+__global__ __launch_bounds__(kTopkThreads) void snap_select_kernel(SnapArgs a, const float* __restrict__ pooled,
                                                                    int32_t* __restrict__ kept_idx,
-                                                                   int32_t* __restrict__ kept_len, int Hkv, int N,
-                                                                   int W, int R) {
+                                                                   int32_t* __restrict__ kept_len) {
   __shared__ TopkShared sm;
   const int b = blockIdx.y, g = blockIdx.x;
-  const int n = lens[b];
-  const int L = n - W;
-  const int cap = R + W;
-  int32_t* out = kept_idx + ((int64_t)b * Hkv + g) * cap;
-  if (L <= R) {
+  const int n = a.lens[b];
+  const int cap = a.kcap, R = a.R;
+  int lo, hi;
+  snap_candidates(a, n, lo, hi);
+  int32_t* out = kept_idx + ((int64_t)b * a.Hkv + g) * cap;
+  if (hi - lo <= R) {
     for (int i = threadIdx.x; i < cap; i += blockDim.x) out[i] = i < n ? i : -1;
-    if (threadIdx.x == 0) kept_len[(int64_t)b * Hkv + g] = n;
+    if (threadIdx.x == 0) kept_len[(int64_t)b * a.Hkv + g] = n;
     return;
   }
-  for (int i = threadIdx.x; i < W; i += blockDim.x) out[R + i] = L + i;
-  if (threadIdx.x == 0) kept_len[(int64_t)b * Hkv + g] = cap;
-  block_topk<KPT>(pooled + ((int64_t)b * Hkv + g) * N, L, R, out, sm);
+  const int kept = lo + R + (n - hi);
+  for (int i = threadIdx.x; i < lo; i += blockDim.x) out[i] = i;
+  for (int i = threadIdx.x; i < n - hi; i += blockDim.x) out[lo + R + i] = hi + i;
+  for (int i = kept + threadIdx.x; i < cap; i += blockDim.x) out[i] = -1;
+  if (threadIdx.x == 0) kept_len[(int64_t)b * a.Hkv + g] = kept;
+  block_topk<KPT>(pooled + ((int64_t)b * a.Hkv + g) * a.N + lo, hi - lo, R, out + lo, sm, nullptr, nullptr, 0,
+                  0x7fffffff, lo);
 }
 
 hipError_t launch_snap_select(const SnapArgs& a, const float* pooled, int32_t* kept_idx, int32_t* kept_len,
@@ -345,8 +350,7 @@ hipError_t launch_snap_select(const SnapArgs& a, const float* pooled, int32_t* k
   switch (pick_kpt(a.N - a.W)) {
 #define SE_K(K)                                                                                                   \
   case K:                                                                                                         \
-    hipLaunchKernelGGL(snap_select_kernel<K>, grid, dim3(kTopkThreads), 0, st, pooled, a.lens, kept_idx, kept_len, \
-                       a.Hkv, a.N, a.W, a.R);                                                                     \
+    hipLaunchKernelGGL(snap_select_kernel<K>, grid, dim3(kTopkThreads), 0, st, a, pooled, kept_idx, kept_len);     \
     break;
     SE_K(1) SE_K(2) SE_K(4) SE_K(8) SE_K(16) SE_K(32) SE_K(64)
 #undef SE_K

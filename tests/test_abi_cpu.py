@@ -11,6 +11,8 @@ import pytest
 import sparse_kv_long_amd as se
 
 FAKE = 0x10000  # a 256-byte aligned non-null address; never dereferenced on these paths
+OUT1 = 1 << 44  # far from FAKE: output buffers that overlap no input
+OUT2 = 1 << 45
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +29,7 @@ def test_every_header_function_is_exported_and_wrapped(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert se.se_version() == 200
+    assert se.se_version() == 300
     assert se.se_status_string(0) == "ok"
     assert "invalid" in se.se_status_string(1)
     assert "unsupported" in se.se_status_string(2)
@@ -38,7 +40,7 @@ def test_version_and_status_strings(lib):
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(se.KvLayout) == 6 * 4 + 3 * 8
     assert ctypes.sizeof(se.DecodeParams) == 10 * 4
-    assert ctypes.sizeof(se.SnapKVParams) == 10 * 4
+    assert ctypes.sizeof(se.SnapKVParams) == 14 * 4
 
 
 def rc_decode(layout, params, **ptrs):
@@ -129,7 +131,15 @@ def test_decode_misaligned_and_workspace():
     (lambda p: setattr(p, "pool_kernel", 0), se.SE_EINVAL),
     (lambda p: setattr(p, "pool_kernel", 131), se.SE_EUNSUPPORTED),
     (lambda p: setattr(p, "window", 0), se.SE_EINVAL),
-    (lambda p: setattr(p, "window", 65), se.SE_EUNSUPPORTED),
+    (lambda p: setattr(p, "window", 129), se.SE_EUNSUPPORTED),
+    (lambda p: setattr(p, "sink", -1), se.SE_EINVAL),
+    (lambda p: setattr(p, "recent", -1), se.SE_EINVAL),
+    (lambda p: setattr(p, "recent", 64), se.SE_EINVAL),  # kept capacity 128 > out_capacity 96
+    (lambda p: setattr(p, "sink", 1), se.SE_EINVAL),
+    (lambda p: (setattr(p, "interval_begin", 5), setattr(p, "interval_end", 5)), se.SE_EINVAL),
+    (lambda p: (setattr(p, "interval_begin", 0), setattr(p, "interval_end", 1001)), se.SE_EINVAL),
+    (lambda p: setattr(p, "interval_begin", 3), se.SE_EINVAL),  # a begin without an end
+    (lambda p: (setattr(p, "interval_begin", 100), setattr(p, "interval_end", 900)), se.SE_EINVAL),
     (lambda p: setattr(p, "budget", 0), se.SE_EINVAL),
     (lambda p: setattr(p, "out_capacity", 95), se.SE_EINVAL),
     (lambda p: setattr(p, "head_dim", 96), se.SE_EUNSUPPORTED),
@@ -140,7 +150,7 @@ def test_decode_misaligned_and_workspace():
 def test_snapkv_argument_errors(mutate, code):
     p = se.snapkv_params(2, 8, 2, 128, 1000, 32, 7, 64, 96)
     mutate(p)
-    rc = se.lib().se_snapkv_compact(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+    rc = se.lib().se_snapkv_compact(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, OUT1, OUT2, FAKE, FAKE, FAKE, 1 << 40,
                                     None)
     assert rc == code
 
@@ -148,9 +158,22 @@ def test_snapkv_argument_errors(mutate, code):
 def test_snapkv_pointer_and_workspace_errors():
     p = se.snapkv_params(2, 8, 2, 128, 1000, 32, 7, 64, 96)
     f = se.lib().se_snapkv_compact
-    assert f(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == se.SE_EINVAL
-    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == se.SE_EWORKSPACE
-    assert f(ctypes.byref(p), FAKE, FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == se.SE_EINVAL
+    assert f(ctypes.byref(p), None, FAKE, FAKE, FAKE, OUT1, OUT2, FAKE, FAKE, FAKE, 1 << 40, None) == se.SE_EINVAL
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, OUT1, OUT2, FAKE, FAKE, FAKE, 16, None) == se.SE_EWORKSPACE
+    assert f(ctypes.byref(p), FAKE, FAKE + 8, FAKE, FAKE, OUT1, OUT2, FAKE, FAKE, FAKE, 1 << 40, None) == se.SE_EINVAL
+    # outputs that overlap an input: the compaction would read rows it overwrites
+    assert f(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, OUT2, FAKE, FAKE, FAKE, 1 << 40, None) == se.SE_EINVAL
+    in_bytes = 2 * 2 * 1000 * 128 * 2
+    assert f(ctypes.byref(p), FAKE, FAKE, OUT2 + 4096, FAKE, OUT1, OUT2, FAKE, FAKE, FAKE, 1 << 40, None) \
+        == se.SE_EINVAL
+    assert f(ctypes.byref(p), FAKE, FAKE, OUT1 + 2 * 2 * 96 * 128 * 2, FAKE, OUT1, OUT1 - in_bytes, FAKE, FAKE, FAKE,
+             16, None) == se.SE_EWORKSPACE  # adjacent, not overlapping
+    # re-eviction needs the positions
+    g = se.lib().se_snapkv_recompact
+    assert g(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, OUT1, OUT2, FAKE, FAKE, FAKE, 1 << 40, None) \
+        == se.SE_EINVAL
+    assert g(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, OUT1, OUT2, FAKE, FAKE, FAKE, 16, None) \
+        == se.SE_EWORKSPACE
     assert se.lib().se_maxpool1d(ctypes.byref(p), None, FAKE, FAKE, None) == se.SE_EINVAL
     assert se.lib().se_snapkv_select(ctypes.byref(p), FAKE, None, FAKE, FAKE, None) == se.SE_EINVAL
     assert se.lib().se_compact(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == se.SE_EINVAL
@@ -162,3 +185,47 @@ def test_product_path_does_not_import_the_oracle():
     for f in list(pkg.glob("*.py")) + list(pkg.glob("csrc/*")):
         text = f.read_text()
         assert "oracle" not in text.replace("oracle-free", ""), f
+
+
+@pytest.mark.parametrize("sink,recent,interval,budget,W,N", [
+    (0, 0, None, 64, 32, 1000), (16, 64, None, 4096, 16, 32768), (0, 4096, None, 4096, 128, 32768),
+    (64, 512, None, 100, 32, 8192), (0, 0, (100, 900), 50, 32, 1000), (5, 70, (2, 30), 7, 8, 1000),
+])
+def test_kept_capacity_matches_oracle(sink, recent, interval, budget, W, N):
+    import oracle
+    want = oracle.eviction_kept_capacity(N, W, budget, sink, recent, interval)
+    p = se.snapkv_params(2, 8, 2, 128, N, W, 7, budget, want, sink=sink, recent=recent,
+                         interval=interval or (0, 0))
+    assert se.se_snapkv_kept_capacity(p) == want
+    p.out_capacity = want - 1
+    with pytest.raises(se.SEError):
+        se.se_snapkv_kept_capacity(p)
+
+
+@pytest.mark.parametrize("L,R,a,z", [
+    (3, 10, 0.6, 0.2), (3, 7, 0.5, 0.1), (47, 4096, 0.6, 0.01), (36, 7987, 0.6, 0.0154712), (1, 4096, 0.6, 0.01),
+    (8, 100, 0.3, 0.3), (40, 2048, 0.01, 0.6), (96, 20000, 0.123456789, 0.987654321), (5, 1, 0.999, 0.001),
+    (4096, 16, 1.0, 0.5),
+])
+def test_pyramid_budgets_match_oracle(L, R, a, z):
+    import oracle
+    assert se.se_pyramid_budgets(L, R, a, z) == oracle.pyramid_budgets(L, R, a, z)
+
+
+def test_pyramid_budgets_random_match_oracle():
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        L, R = int(rng.integers(1, 130)), int(rng.integers(1, 30000))
+        a, z = float(rng.uniform(0.001, 2.0)), float(rng.uniform(0.001, 2.0))
+        assert se.se_pyramid_budgets(L, R, a, z) == oracle.pyramid_budgets(L, R, a, z), (L, R, a, z)
+
+
+def test_pyramid_budget_errors():
+    for args, code in [((0, 10, 0.6, 0.1), se.SE_EINVAL), ((3, 0, 0.6, 0.1), se.SE_EINVAL),
+                       ((3, 10, 0.0, 0.1), se.SE_EINVAL), ((3, 10, 0.6, -1.0), se.SE_EINVAL),
+                       ((3, 10, float("nan"), 0.1), se.SE_EINVAL), ((5000, 10, 0.6, 0.1), se.SE_EUNSUPPORTED)]:
+        out = (ctypes.c_int32 * 8)()
+        assert se.lib().se_pyramid_budgets(*args, out) == code
+    assert se.lib().se_pyramid_budgets(3, 10, 0.6, 0.1, None) == se.SE_EINVAL

@@ -274,22 +274,26 @@ def bench_snapkv(args, wl):
     x = make_snapkv_inputs(wl, dev)
     torch.cuda.synchronize()
     gen_s = time.time() - t0
-    B, Hq, H, D, W, R, C = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window, wl.budget, wl.out_capacity
+    B, Hq, H, D, W, R = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window, wl.budget
     n = wl.prompt
-    p = se.snapkv_params(B, Hq, H, D, n, W, wl.pool_kernel, R, C, wl.scale)
+    S = wl.decode_steps
+    p = se.snapkv_params(B, Hq, H, D, n, W, wl.pool_kernel, R, 1 << 30, wl.scale, sink=wl.sink, recent=wl.recent,
+                         interval=wl.interval)
+    kcap = se.se_snapkv_kept_capacity(p)
+    C = (kcap + S + 15) // 16 * 16  # kept rows plus the decode steps, whole pages
+    p.out_capacity = C
     ws = torch.empty(se.se_snapkv_workspace_size(p), dtype=torch.uint8, device=dev)
     k_out = torch.zeros((B, H, C, D), dtype=torch.bfloat16, device=dev)
     v_out = torch.zeros((B, H, C, D), dtype=torch.bfloat16, device=dev)
-    kept = torch.empty((B, H, R + W), dtype=torch.int32, device=dev)
+    kept = torch.empty((B, H, kcap), dtype=torch.int32, device=dev)
     klen = torch.empty((B, H), dtype=torch.int32, device=dev)
     se.se_snapkv_compact(p, x["q_win"], x["k"], x["v"], x["prompt_lens"], k_out, v_out, kept, klen, ws)
     torch.cuda.synchronize()
     kl = int(klen[0, 0])
-    assert (klen == kl).all() and kl == R + W
+    assert (klen == kl).all() and kl <= kcap
     # the decode steps' tokens go in at rows kl..kl+steps-1 (the engine's
     # append); the eviction writes only rows < kept_len, so they are placed
     # once, outside the timing
-    S = wl.decode_steps
     k_out[:, :, kl:kl + S] = x["k_steps"].permute(1, 2, 0, 3)
     v_out[:, :, kl:kl + S] = x["v_steps"].permute(1, 2, 0, 3)
     MP = C // 16
@@ -344,20 +348,48 @@ def bench_snapkv(args, wl):
                            flush)
     dec_ms, _ = timed_calls(decode_graph, steps, 1, None)
 
+    # re-eviction after the decode steps (the pages evict again every 1,024
+    # decode steps): the same budget over the kept rows plus the steps, the
+    # last W decode queries as the window, original positions carried through
+    n2 = kl + S
+    p2 = se.snapkv_params(B, Hq, H, D, C, W, wl.pool_kernel, R, 1 << 30, wl.scale, sink=wl.sink,
+                          recent=wl.recent)
+    kcap2 = se.se_snapkv_kept_capacity(p2)
+    p2.out_capacity = (kcap2 + 15) // 16 * 16
+    ws2 = torch.empty(se.se_snapkv_workspace_size(p2), dtype=torch.uint8, device=dev)
+    k2 = torch.zeros((B, H, p2.out_capacity, D), dtype=torch.bfloat16, device=dev)
+    v2 = torch.zeros_like(k2)
+    kept2 = torch.empty((B, H, kcap2), dtype=torch.int32, device=dev)
+    klen2 = torch.empty((B, H), dtype=torch.int32, device=dev)
+    positions = torch.full((B, H, C), -1, dtype=torch.int32, device=dev)
+    positions[:, :, :kl] = kept[:, :, :kl]
+    positions[:, :, kl:n2] = torch.arange(n, n + S, dtype=torch.int32, device=dev)
+    q_win2 = x["q_steps"][S - W:].permute(1, 2, 0, 3).contiguous() if S >= W else None
+    lens2 = torch.full((B,), n2, dtype=torch.int32, device=dev)
+    re_ms = None
+    if q_win2 is not None:
+        re_ms, _ = timed_calls(lambda i: se.se_snapkv_recompact(p2, q_win2, k_out, v_out, lens2, positions, k2, v2,
+                                                                kept2, klen2, ws2), steps, 1, flush)
+
     t_whole = float(np.mean(whole_ms)) * 1e-3
     tokens_s = B * S / t_whole
     # algorithmic bytes: the window queries, K once, the kept K/V rows read and
     # written, the kept ids; then per decode step the attended rows, q and out
     rows_dec = sum(kl + s + 1 for s in range(S))
-    b_evict = B * Hq * W * D * 2 + B * H * n * D * 2 + 2 * 2 * B * H * kl * D * 2 + B * H * (R + W) * 4
+    b_evict = B * Hq * W * D * 2 + B * H * n * D * 2 + 2 * 2 * B * H * kl * D * 2 + B * H * kl * 4
     b_dec = B * H * rows_dec * 2 * D * 2 + S * (B * Hq * D * 2 + B * Hq * D * 4)
     b_votes = B * Hq * W * D * 2 + B * H * n * D * 2 + B * H * n * 4
-    flops_votes = 2 * 2 * B * Hq * W * n * D  # two passes over the window x context scores
+    # window x context scores: pass 1 over every key, pass 2 over the columns
+    # whose votes the selection reads (the candidates plus the pooling halo)
+    ib, ie = wl.interval if wl.interval[1] else (0, n)
+    lo, hi = max(wl.sink, ib), min(n - max(wl.recent, W), ie)
+    vcols = min(hi + wl.pool_kernel // 2, n - W) - max(lo - wl.pool_kernel // 2, 0)
+    flops_votes = 2 * B * Hq * W * D * (n + (n - W))  # se_snapkv_votes scores every prefix column
     t_votes = float(np.mean(vo_ms)) * 1e-3
     t_ev = float(np.mean(ev_ms)) * 1e-3
     t_dec = float(np.mean(dec_ms)) * 1e-3
     result = {
-        "metric": "SnapKV eviction + decode tokens/s over the compacted cache, 32K prompt, 1 GPU",
+        "metric": f"{wl.method} eviction + decode tokens/s over the compacted cache, 32K prompt, 1 GPU",
         "value": round(tokens_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -369,12 +401,16 @@ def bench_snapkv(args, wl):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl.name, "batch": B, "prompt": n, "num_q_heads": Hq, "num_kv_heads": H,
-                   "head_dim": D, "window": W, "pool_kernel": wl.pool_kernel, "budget": R, "decode_steps": S},
+        "config": {"workload": wl.name, "method": wl.method, "batch": B, "prompt": n, "num_q_heads": Hq,
+                   "num_kv_heads": H, "head_dim": D, "window": W, "pool_kernel": wl.pool_kernel, "budget": R,
+                   "sink": wl.sink, "recent": wl.recent, "interval": list(wl.interval), "kept_tokens": kl,
+                   "decode_steps": S},
         "effective_hbm_gbps": round((b_evict + b_dec) / t_whole / 1e9, 1),
         "algorithmic_bytes_per_step": b_evict + b_dec,
         "pieces_ms": {"eviction": round(t_ev * 1e3, 4), "votes_only": round(t_votes * 1e3, 4),
-                      "decode_steps_total": round(t_dec * 1e3, 4), "decode_step_mean": round(t_dec * 1e3 / S, 5)},
+                      "decode_steps_total": round(t_dec * 1e3, 4), "decode_step_mean": round(t_dec * 1e3 / S, 5),
+                      "reeviction_after_steps": None if re_ms is None else round(float(np.mean(re_ms)), 4)},
+        "eviction_vote_columns_pass2": vcols,
         "eviction_gbps": round(b_evict / t_ev / 1e9, 1),
         "decode_gbps_cache_resident": round(b_dec / t_dec / 1e9, 1),
         "roofline": {"kernel": "snapkv votes (row statistics + votes, MFMA)", "bound": "hbm",
@@ -415,7 +451,8 @@ def cpu_baseline_snapkv(wl, x, seconds):
         with threadpool_limits(1):
             t0 = time.perf_counter()
             Sv, _, _ = oracle.snapkv_unit_votes(oracle.bf16_to_f64(qw), oracle.bf16_to_f64(kb), n, wl.scale)
-            keep = oracle.snapkv_unit_keep(oracle.maxpool1d(Sv, wl.pool_kernel), n, W, R)
+            keep = oracle.eviction_unit_keep(oracle.maxpool1d(Sv, wl.pool_kernel), n, W, R, wl.sink, wl.recent,
+                                             wl.interval if wl.interval[1] else None)
             kc = np.concatenate([kb[keep], ks])[None]
             vc = np.concatenate([vb[keep], vs])[None]
             for s in range(S):

@@ -83,6 +83,10 @@ class SnapKVWorkload:
     decode_steps: int
     seed: int = 0
     ragged_lo: int = 0
+    method: str = "SnapKV"
+    sink: int = 0                 # leading tokens always kept
+    recent: int = 0               # trailing tokens always kept (at least the window)
+    interval: tuple = (0, 0)      # history span that may be pruned; (0, 0): the whole prompt
 
     @property
     def group(self) -> int:
@@ -94,6 +98,7 @@ class SnapKVWorkload:
 
     @property
     def out_capacity(self) -> int:
+        # for the plain SnapKV shapes (no sink, recent or interval)
         # kept rows plus room for the decode steps, rounded up to whole pages
         need = self.budget + self.window + self.decode_steps
         return (need + PAGE - 1) // PAGE * PAGE
@@ -108,10 +113,19 @@ TINY_QUEST = QuestWorkload("tiny_quest_4k", 1, 4, 1, 64, 64, 4096, 32, "heavy", 
 QWEN3_4B_32K = QuestWorkload("gqa32x8_d128_32k_b8", 8, 32, 8, 128, 128, 32768, 128, "outlier", seed=1002)
 QWEN3_30B_128K = QuestWorkload("gqa32x4_d128_128k_b32", 32, 32, 4, 128, 128, 131072, 256, "zipf", seed=1003)
 SNAPKV_32K = SnapKVWorkload("snapkv_gqa32x8_d128_32k_b16", 16, 32, 8, 128, 32768, 32, 7, 2048, 64, seed=1004)
+# Eviction-family legs on the SnapKV workload's shape and values (same seed):
+# H2O with Table 8's settings (8,192 prefill tokens split by the recent ratio
+# 0.5, a 128-token scoring window, no pooling), and prefix-cache pruning
+# (Figure 4) of a 24K-token history span [4096, 28672) to 2048 tokens.
+H2O_32K = SnapKVWorkload("h2o_gqa32x8_d128_32k_b16", 16, 32, 8, 128, 32768, 128, 1, 4096, 64, seed=1004,
+                         method="H2O", recent=4096)
+PRUNE_32K = SnapKVWorkload("prune_gqa32x8_d128_32k_b16", 16, 32, 8, 128, 32768, 32, 7, 2048, 64, seed=1004,
+                           method="prefix-cache pruning", interval=(4096, 28672))
 MLA_RAGGED = QuestWorkload("mla576_h32_ragged16k-128k_b16", 16, 32, 1, 576, 512, 131072, 256, "none",
                            v_is_k_prefix=True, ragged_lo=16384, seed=1005)
 
-WORKLOADS = {w.name: w for w in (TINY_QUEST, QWEN3_4B_32K, QWEN3_30B_128K, SNAPKV_32K, MLA_RAGGED)}
+WORKLOADS = {w.name: w for w in (TINY_QUEST, QWEN3_4B_32K, QWEN3_30B_128K, SNAPKV_32K, MLA_RAGGED, H2O_32K,
+                                 PRUNE_32K)}
 
 
 def _gen(device, seed: int, tag: int) -> torch.Generator:

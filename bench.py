@@ -46,23 +46,30 @@ def parse():
     return ap.parse_args()
 
 
-def kernel_sources_hash() -> str:
+# Source files each recorded kernel is built from (beside the shared headers
+# and the build flags): a counter record stays valid while these are unchanged.
+KERNEL_SOURCES = {"quest_score": ["quest.hip"], "topk_pages": ["topk.hip"], "decode": ["decode.hip"],
+                  "merge": ["decode.hip"], "snapkv_votes": ["snapkv.hip"]}
+
+
+def kernel_sources_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "sparse_kv_long_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    pkg = os.path.join(ROOT, "sparse_kv_long_amd")
+    files = [os.path.join("csrc", f) for f in KERNEL_SOURCES[kernel] + ["common.h", "se_internal.h"]] + ["build.py"]
+    for f in files:
         h.update(f.encode())
-        h.update(open(os.path.join(csrc, f), "rb").read())
+        h.update(open(os.path.join(pkg, f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def traffic_record(kernel: str, workload: str):
     """HBM bytes per launch measured with rocprofv3 counters, if they were
-    taken for this workload on the current kernel sources (else None)."""
+    taken for this workload on the kernel's current sources (else None)."""
     path = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(f"{kernel}@{workload}")
-    if not rec or rec.get("sources_hash") != kernel_sources_hash():
+    if not rec or rec.get("sources_hash") != kernel_sources_hash(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -210,12 +217,25 @@ def main():
                       "decode_and_merge": round(float(np.mean(k34_ms)), 4)},
         "roofline": roofline,
         "decode_kernel_gbps": round(k34_gbps, 1),
+        # the bytes the step's kernels actually move (rocprofv3 FETCH_SIZE +
+        # WRITE_SIZE per launch, calibrated), over the measured step time
+        **counted_bytes(wl.name, t_step, forced),
         "input_generation_s": round(gen_s, 1),
     }
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, qs, args.cpu_seconds, topk, sink, recent)
     print(json.dumps(result))
+
+
+def counted_bytes(workload: str, t_step: float, forced: bool) -> dict:
+    recs = [traffic_record(k, workload) for k in ("quest_score", "topk_pages", "decode", "merge")]
+    if forced or any(r is None for r in recs):
+        return {"counted_hbm_bytes_per_step": None, "counted_hbm_gbps": None, "pct_peak_hbm_counted": None}
+    total = int(sum(recs))
+    gbps = total / t_step / 1e9
+    return {"counted_hbm_bytes_per_step": total, "counted_hbm_gbps": round(gbps, 1),
+            "pct_peak_hbm_counted": round(100 * gbps / HBM_PEAK_GBPS, 2)}
 
 
 def timed_calls(fn, count, warm, flush):

@@ -20,8 +20,14 @@
 //          vote 2^(z - c_r) summed over rows is lane-local.  Only prefix keys
 //          j < L need votes and every window row sees all of them, so pass 2
 //          needs no causal mask.
-// One block handles a strided set of 32-key tiles of one (request, KV head,
-// row group of up to 128 rows), keeping the rows' q fragments in registers.
+// Rows come in groups of up to 128 (four 32-row MFMA tiles), whose q
+// fragments a wave keeps in registers.  With one row group (SnapKV's 32-row
+// window and small groups) a block's four waves take different key tiles of
+// one (request, KV head).  With two to eight row groups (H2O's 128-row
+// window) the block's waves are the row groups and walk the same key tiles
+// together, so each tile comes from HBM once and the other waves find it in
+// the CU's caches (one block per row group read every key once per group,
+// measured at eight times the algorithmic bytes for four groups).
 #include "common.h"
 #include "se_internal.h"
 
@@ -31,7 +37,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kRowsPerGroup = 128;
-constexpr int kSnapWaves = 4;
+constexpr int kSnapWaves = 4;     // waves per block with one row group
+constexpr int kMaxRgWaves = 8;    // row groups a block can take as its waves
 
 __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, const f32x16_t& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -63,17 +70,28 @@ __device__ __forceinline__ void vote_span(const SnapArgs& a, int n, int& vlo, in
 struct SnapGeom {
   int rows;   // G*W
   int nrg;    // row groups of up to 128 rows
-  int nblk;   // blocks per (request, KV head, row group)
-  int slots;  // row-stat partials per (request, KV head, row group) = nblk * waves
+  bool rgw;   // the block's waves are the row groups (2 <= nrg <= kMaxRgWaves)
+  int nblk;   // blocks per (request, KV head[, row group])
+  int slots;  // row-stat partials per (request, KV head, row group): key-tile walkers
 };
 
 static SnapGeom snap_geom(const SnapArgs& a) {
   SnapGeom s;
   s.rows = (a.Hq / a.Hkv) * a.W;
   s.nrg = (s.rows + kRowsPerGroup - 1) / kRowsPerGroup;
+  s.rgw = s.nrg >= 2 && s.nrg <= kMaxRgWaves;
+  const int tiles = (a.N + 31) / 32;
+  if (s.rgw) {
+    const int units = a.B * a.Hkv;
+    int nblk = (2048 + units * s.nrg - 1) / (units * s.nrg);  // about 2048 waves in flight
+    if (nblk > tiles) nblk = tiles;
+    if (nblk < 1) nblk = 1;
+    s.nblk = nblk;
+    s.slots = nblk;
+    return s;
+  }
   const int units = a.B * a.Hkv * s.nrg;
   int nblk = (512 + units - 1) / units;  // about 2048 waves in flight
-  const int tiles = (a.N + 31) / 32;
   const int maxblk = (tiles + kSnapWaves - 1) / kSnapWaves;
   if (nblk > maxblk) nblk = maxblk;
   if (nblk < 1) nblk = 1;
@@ -141,19 +159,24 @@ __device__ __forceinline__ void load_k_frags(const uint16_t* kbase, int kt, int 
 
 // ---------------------------------------------------------------------------
 // Pass 1: partial row max / sum of 2^z (log2-domain logits).
-// Grid (nblk, Hkv * nrg, B), 4 waves.  Wave slot = blockIdx.x*4 + wave.
+// Grid (nblk, Hkv * nrg, B), 4 waves, wave slot = blockIdx.x*4 + wave; or
+// with RGW grid (nblk, Hkv, B), nrg waves, wave = row group, slot = blockIdx.x.
 // ---------------------------------------------------------------------------
-template <int D, int NRT>
-__global__ __launch_bounds__(256) void snap_rowstats_kernel(SnapArgs a, float* __restrict__ row_part, int nrg,
-                                                            int slots, int skip_kept, float scale2) {
-  const int b = blockIdx.z, g = blockIdx.y / nrg, rg = blockIdx.y % nrg;
+template <int D, int NRT, bool RGW>
+__global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_rowstats_kernel(SnapArgs a,
+                                                                                    float* __restrict__ row_part,
+                                                                                    int nrg, int slots, int skip_kept,
+                                                                                    float scale2) {
+  const int b = blockIdx.z;
+  const int g = RGW ? blockIdx.y : blockIdx.y / nrg;
+  const int rg = RGW ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : blockIdx.y % nrg;
   const int n = a.lens[b];
   const int L = n - a.W;
   if (L <= 0 || (skip_kept && nothing_dropped(a, n))) return;
   const int G = a.Hq / a.Hkv;
   const int rows = G * a.W;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = blockIdx.x * kSnapWaves + wave;
+  const int slot = RGW ? (int)blockIdx.x : (int)blockIdx.x * kSnapWaves + wave;
 
   uint4 qf[NRT][D / 16];
   load_q_frags<D, NRT>(a, b, g, rg, rows, qf);
@@ -247,32 +270,40 @@ __global__ __launch_bounds__(128) void snap_rowmerge_kernel(SnapArgs a, const fl
 }
 
 // ---------------------------------------------------------------------------
-// Pass 2: votes of prefix keys.  Grid (nblk, Hkv * nrg, B), 4 waves.
+// Pass 2: votes of prefix keys.  Grid and waves as pass 1.
 // votes layout [nrg, B, Hkv, N].
 // ---------------------------------------------------------------------------
-template <int D, int NRT>
-__global__ __launch_bounds__(256) void snap_votes_kernel(SnapArgs a, const float* __restrict__ row_c,
-                                                         float* __restrict__ votes, int nrg, int slots, int skip_kept,
-                                                         float scale2) {
-  __shared__ float c_lds[kRowsPerGroup];
-  const int b = blockIdx.z, g = blockIdx.y / nrg, rg = blockIdx.y % nrg;
+template <int D, int NRT, bool RGW>
+__global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_votes_kernel(SnapArgs a,
+                                                                                 const float* __restrict__ row_c,
+                                                                                 float* __restrict__ votes, int nrg,
+                                                                                 int slots, int skip_kept,
+                                                                                 float scale2) {
+  __shared__ float c_lds[RGW ? kMaxRgWaves : 1][kRowsPerGroup];
+  const int b = blockIdx.z;
+  const int g = RGW ? blockIdx.y : blockIdx.y / nrg;
+  const int rg = RGW ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : blockIdx.y % nrg;
   const int n = a.lens[b];
   const int L = n - a.W;
   if (L <= 0 || (skip_kept && nothing_dropped(a, n))) return;
   const int G = a.Hq / a.Hkv;
   const int rows = G * a.W;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = blockIdx.x * kSnapWaves + wave;
+  const int slot = RGW ? (int)blockIdx.x : (int)blockIdx.x * kSnapWaves + wave;
   // columns whose votes are needed: the whole prefix, or (when selecting)
   // the candidates plus the pooling halo
   int vlo = 0, vhi = L;
   if (skip_kept) vote_span(a, n, vlo, vhi);
-  for (int r = threadIdx.x; r < kRowsPerGroup; r += blockDim.x) {
-    const int gr = rg * kRowsPerGroup + r;
+  // normalisers of the block's row groups: all nrg with RGW, else its one
+  const int rg0 = RGW ? 0 : rg, nrg_blk = RGW ? nrg : 1;
+  for (int r = threadIdx.x; r < nrg_blk * kRowsPerGroup; r += blockDim.x) {
+    const int gr = (rg0 + r / kRowsPerGroup) * kRowsPerGroup + r % kRowsPerGroup;
     // rows past G*W get +inf so their weight 2^(z - c) is 0
-    c_lds[r] = gr < rows ? row_c[((int64_t)b * a.Hq + g * G + gr / a.W) * a.W + gr % a.W] : __builtin_inff();
+    c_lds[r / kRowsPerGroup][r % kRowsPerGroup] =
+        gr < rows ? row_c[((int64_t)b * a.Hq + g * G + gr / a.W) * a.W + gr % a.W] : __builtin_inff();
   }
   __syncthreads();
+  const float* cw = c_lds[RGW ? rg : 0];
 
   uint4 qf[NRT][D / 16];
   load_q_frags<D, NRT>(a, b, g, rg, rows, qf);
@@ -294,7 +325,7 @@ __global__ __launch_bounds__(256) void snap_votes_kernel(SnapArgs a, const float
       for (int ks = 0; ks < D / 16; ++ks) acc = mfma32(qf[rt][ks], kf[ks], acc);
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 c4 = *reinterpret_cast<const float4*>(&c_lds[rt * 32 + 8 * r4 + 4 * (lane >> 5)]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&cw[rt * 32 + 8 * r4 + 4 * (lane >> 5)]);
         vote += __builtin_amdgcn_exp2f(acc[4 * r4 + 0] * scale2 - c4.x);
         vote += __builtin_amdgcn_exp2f(acc[4 * r4 + 1] * scale2 - c4.y);
         vote += __builtin_amdgcn_exp2f(acc[4 * r4 + 2] * scale2 - c4.z);
@@ -307,12 +338,13 @@ __global__ __launch_bounds__(256) void snap_votes_kernel(SnapArgs a, const float
   }
 }
 
-template <int D, int NRT>
+template <int D, int NRT, bool RGW>
 static hipError_t launch_votes_t(const SnapArgs& a, const SnapWork& w, const SnapGeom& s, int skip, float* votes,
                                  hipStream_t st) {
   const float scale2 = a.scale * kLog2e;
-  dim3 grid(s.nblk, a.Hkv * s.nrg, a.B);
-  hipLaunchKernelGGL((snap_rowstats_kernel<D, NRT>), grid, dim3(256), 0, st, a, w.row_part, s.nrg, s.slots, skip,
+  const dim3 grid(s.nblk, RGW ? a.Hkv : a.Hkv * s.nrg, a.B);
+  const dim3 block(RGW ? 64 * s.nrg : 256);
+  hipLaunchKernelGGL((snap_rowstats_kernel<D, NRT, RGW>), grid, block, 0, st, a, w.row_part, s.nrg, s.slots, skip,
                      scale2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -320,7 +352,7 @@ static hipError_t launch_votes_t(const SnapArgs& a, const SnapWork& w, const Sna
                      skip);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((snap_votes_kernel<D, NRT>), grid, dim3(256), 0, st, a, w.row_c, votes, s.nrg, s.slots, skip,
+  hipLaunchKernelGGL((snap_votes_kernel<D, NRT, RGW>), grid, block, 0, st, a, w.row_c, votes, s.nrg, s.slots, skip,
                      scale2);
   return hipGetLastError();
 }
@@ -331,8 +363,13 @@ hipError_t launch_snap_votes(const SnapArgs& a, const SnapWork& w, bool skip_kep
   const SnapGeom s = snap_geom(a);
   const int nrt = (s.nrg > 1 ? kRowsPerGroup : s.rows + 31) / 32;  // row tiles per group
   const int skip = skip_kept ? 1 : 0;
+  if (s.rgw) {  // several full row groups: four row tiles per wave
+    if (a.D == 128) return launch_votes_t<128, 4, true>(a, w, s, skip, votes_out, st);
+    if (a.D == 64) return launch_votes_t<64, 4, true>(a, w, s, skip, votes_out, st);
+    return hipErrorInvalidValue;
+  }
 #define SE_V(DD, RT) \
-  if (a.D == DD && nrt == RT) return launch_votes_t<DD, RT>(a, w, s, skip, votes_out, st);
+  if (a.D == DD && nrt == RT) return launch_votes_t<DD, RT, false>(a, w, s, skip, votes_out, st);
   SE_V(128, 1) SE_V(128, 2) SE_V(128, 3) SE_V(128, 4) SE_V(64, 1) SE_V(64, 2) SE_V(64, 3) SE_V(64, 4)
 #undef SE_V
   return hipErrorInvalidValue;

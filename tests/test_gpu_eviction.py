@@ -24,6 +24,12 @@ CASES = {
                     [1500, 900, 401], 0, 200, None),
     "h2o_w128_g8_d64": (SnapKVWorkload("e_h2o64", 2, 8, 1, 64, 1200, 128, 1, 150, 0, seed=43),
                         [1200, 640], 0, 150, None),
+    # edge lengths: empty, shorter than the window, exactly the window, exactly
+    # sink + recent (nothing to choose from), one candidate past the budget
+    "edges_sink_recent": (SnapKVWorkload("e_edge", 7, 8, 2, 128, 400, 16, 5, 30, 0, seed=47),
+                          [0, 9, 16, 48, 78, 79, 400], 8, 40, None),
+    "edges_interval": (SnapKVWorkload("e_edge2", 6, 4, 2, 64, 300, 8, 3, 20, 0, seed=48),
+                       [0, 7, 60, 121, 150, 300], 2, 0, (100, 141)),
     # prefix-cache pruning: only positions 200..699 may go
     "prune_200_700": (SnapKVWorkload("e_prune", 4, 8, 2, 128, 1000, 32, 7, 60, 0, seed=44),
                       [1000, 650, 260, 100], 0, 0, (200, 700)),

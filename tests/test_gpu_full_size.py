@@ -10,7 +10,8 @@ import torch
 
 import oracle
 import sparse_kv_long_amd as se
-from synth import MLA_RAGGED, QWEN3_4B_32K, QWEN3_30B_128K, SNAPKV_32K, make_quest_inputs, make_snapkv_inputs, bf16_bits
+from synth import (H2O_32K, MLA_RAGGED, PRUNE_32K, QWEN3_4B_32K, QWEN3_30B_128K, SNAPKV_32K, make_quest_inputs,
+                   make_snapkv_inputs, bf16_bits)
 from gpu_util import DEV, announce, build_summaries, check_attention, check_selection, layout_for, to_np, workspace
 
 pytestmark = pytest.mark.gpu
@@ -145,3 +146,45 @@ def test_snapkv_full_size_sampled_units():
                 ref = oracle.decode_over_rows(qs[b], ko, vo, int(lens[b]), G, wl.scale)
                 check_attention(o[b], ref, float(np.abs(oracle.bf16_to_f64(vo)).max()), f"snapkv step {s} b{b}")
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("wl", [H2O_32K, PRUNE_32K], ids=lambda w: w.name)
+def test_eviction_family_full_size_sampled_units(wl):
+    """The H2O and prefix-pruning legs at the size the bench runs: counts,
+    forced tokens and bitwise copies on every unit, votes and selection on
+    sampled units against the oracle."""
+    announce(f"full-size eviction {wl.name} seed {wl.seed}")
+    x = make_snapkv_inputs(wl, DEV, with_decode=False)
+    iv = wl.interval if wl.interval[1] else None
+    kcap = oracle.eviction_kept_capacity(wl.prompt, wl.window, wl.budget, wl.sink, wl.recent, iv)
+    p = se.snapkv_params(wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.prompt, wl.window,
+                         wl.pool_kernel, wl.budget, (kcap + 15) // 16 * 16, wl.scale, sink=wl.sink,
+                         recent=wl.recent, interval=wl.interval)
+    assert se.se_snapkv_kept_capacity(p) == kcap
+    ws = workspace(se.se_snapkv_workspace_size(p))
+    B, H, C, D = wl.batch, wl.num_kv_heads, p.out_capacity, wl.head_dim
+    k_out = torch.zeros((B, H, C, D), dtype=torch.bfloat16, device=DEV)
+    v_out = torch.zeros((B, H, C, D), dtype=torch.bfloat16, device=DEV)
+    kept = torch.full((B, H, kcap), 777, dtype=torch.int32, device=DEV)
+    klen = torch.zeros((B, H), dtype=torch.int32, device=DEV)
+    se.se_snapkv_compact(p, x["q_win"], x["k"], x["v"], x["prompt_lens"], k_out, v_out, kept, klen, ws)
+    torch.cuda.synchronize()
+    n = wl.prompt
+    lo, hi = oracle.eviction_candidates(n, wl.window, wl.sink, wl.recent, iv)
+    R = wl.budget
+    K, KL = to_np(kept), to_np(klen)
+    assert hi - lo > R and (KL == lo + R + n - hi).all() and kcap == lo + R + n - hi
+    assert (K[..., :lo] == np.arange(lo)).all() and (K[..., lo + R:] == np.arange(hi, n)).all()
+    assert (np.diff(K, axis=-1) > 0).all()
+    idx = kept.long()
+    for src, dst in ((x["k"], k_out), (x["v"], v_out)):
+        gathered = torch.gather(src, 2, idx[..., None].expand(-1, -1, -1, D))
+        assert torch.equal(gathered.view(torch.int16), dst[:, :, :kcap].view(torch.int16))
+    qb = bf16_bits(x["q_win"])
+    G = wl.group
+    for b, g in ((0, 0), (B - 1, H - 1)):
+        announce(f"{wl.name} unit b{b} g{g}")
+        keys = oracle.bf16_to_f64(bf16_bits(x["k"][b, g]))
+        Sv, _, _ = oracle.snapkv_unit_votes(oracle.bf16_to_f64(qb[b, g * G:(g + 1) * G]), keys, n, wl.scale)
+        pooled = oracle.maxpool1d(Sv, wl.pool_kernel)
+        check_selection(K[b, g, lo:lo + R] - lo, pooled[lo:hi], R, f"{wl.name} b{b} g{g}")

@@ -113,6 +113,26 @@ __device__ __forceinline__ uint4 ldnt16(const void* p) {
 }
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// A raw buffer resource over `bytes` bytes from p (dword 3: the gfx9 untyped
+// 32-bit format).  With bytes = 0 every load through it returns zeros without
+// a memory access, so a prefetch ring can issue a fixed number of loads per
+// step (the compiler then counts them and waits for one tile at a time) and
+// still read nothing past its last page.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, bytes, 0x00020000);
+}
+// 16 bytes at byte offset `off` of the resource, non-temporal.
+__device__ __forceinline__ uint4 ldbuf_nt16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+// 8 bytes at byte offset `off` of the resource.
+__device__ __forceinline__ uint2 ldbuf8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+  return make_uint2(v.x, v.y);
+}
+
 // Order-preserving map of an fp32 to an unsigned key: a > b  <=>  key(a) > key(b)
 // for non-NaN values, with -0 taken as +0 so the two compare equal.
 __device__ __forceinline__ uint32_t float_key(float f) {

@@ -402,15 +402,18 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
   for (int e = 0; e < 4; ++e) roff[e] = (uint32_t)(2 * (8 * col + (4 * kq + e) * ts));
   const uint16_t* kh = a.k + (int64_t)g * hs;
   const uint16_t* vh = a.v + (int64_t)g * hs;
+  // past the wave's last page the ring's loads go through empty resources:
+  // they return zeros and read nothing (a repeat of the last page would be
+  // re-fetched: the page loads are non-temporal)
   auto load = [&](int ii, PageRegs& r) {
     const int64_t pid = pid_lds[w + NW * min(ii, npw - 1)];
     const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane((int)pid) * ps;
-    const char* kp = reinterpret_cast<const char*>(kh + off);
-    const char* vp = reinterpret_cast<const char*>(vh + off);
+    const int span = ii < npw ? 0x7fffffff : 0;
+    const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kh + off, span), rv = buf_rsrc(vh + off, span);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r.k[e] = ldnt16(kp + roff[e]);
+    for (int e = 0; e < 4; ++e) r.k[e] = ldbuf_nt16(rk, roff[e]);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r.v[e] = ldnt16(vp + roff[e]);
+    for (int e = 0; e < 4; ++e) r.v[e] = ldbuf_nt16(rv, roff[e]);
   };
 
   float m_run = -__builtin_inff();  // running max of head col (log2 domain)
@@ -639,11 +642,19 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
     uint4 v[4];
     uint2 r;
   };
-  auto load = [&](int ii, PageRegs& R) {
-    const int64_t off = pid_lds[min(ii, npg - 1)] * ps;
+  // byte offsets inside a page (vrow / rrow above, relative to kb); past the
+  // block's last page the ring's loads go through an empty resource and read
+  // nothing
+  uint32_t voff[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) R.v[e] = ldnt16(vrow + off + e * ts);
-    R.r = *reinterpret_cast<const uint2*>(rrow + off);
+  for (int e = 0; e < 4; ++e) voff[e] = (uint32_t)(2 * ((vrow - kb) + e * ts));
+  const uint32_t roff = (uint32_t)(2 * (rrow - kb));
+  auto load = [&](int ii, PageRegs& R) {
+    const int64_t off = (int64_t)__builtin_amdgcn_readfirstlane((int)pid_lds[min(ii, npg - 1)]) * ps;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(kb + off, ii < npg ? 0x7fffffff : 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) R.v[e] = ldbuf_nt16(rs, voff[e]);
+    R.r = ldbuf8(rs, roff);
   };
 
   float m_run[NHT], l_run[NHT];

@@ -303,14 +303,28 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
       __builtin_amdgcn_wave_barrier();
       finish(acc, start + 16 * t, end);
     };
+    // two tiles per step while a third follows, then the one or two left
+    // without prefetch: every tile is fetched once (a clamped prefetch past
+    // the last tile re-fetched it, the loads being non-temporal), and inside
+    // the loop the loads stay unconditional, so the compiler waits for one
+    // tile at a time instead of draining both
     load(0, dA);
-    for (int t = 0; t < ntile; t += 2) {
-      load(min(t + 1, ntile - 1), dB);
+    int t = 0;
+    for (; t + 2 < ntile; t += 2) {
+      load(t + 1, dB);
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
       score(t, dA);
-      load(min(t + 2, ntile - 1), dA);
+      load(t + 2, dA);
       __builtin_amdgcn_sched_barrier(0);
-      if (t + 1 < ntile) score(t + 1, dB);
+      score(t + 1, dB);
+    }
+    if (t + 1 < ntile) {
+      load(t + 1, dB);
+      __builtin_amdgcn_sched_barrier(0);
+      score(t, dA);
+      score(t + 1, dB);
+    } else {
+      score(t, dA);
     }
   }
 

@@ -92,6 +92,9 @@ def main():
     from synth import WORKLOADS, SnapKVWorkload, make_quest_inputs
 
     wl = WORKLOADS[args.workload]
+    if isinstance(wl, SnapKVWorkload) and wl.layers > 1:
+        bench_pyramid(args, wl)
+        return
     if isinstance(wl, SnapKVWorkload):
         bench_snapkv(args, wl)
         return
@@ -448,7 +451,138 @@ def bench_snapkv(args, wl):
     print(json.dumps(result))
 
 
-def cpu_baseline_snapkv(wl, x, seconds):
+def bench_pyramid(args, wl):
+    """PyramidKV over a slice of `wl.layers` layers: each layer evicts the
+    32K prompt with its own budget from se_pyramid_budgets (the same sink,
+    recent and window in every layer), then the decode steps run through
+    every layer's retained cache.  One step = every layer's eviction + every
+    layer's decode steps; tokens/s counts the decode tokens produced (each
+    passes through all the layers).  The layers share one synthetic cache."""
+    import numpy as np
+    import torch
+
+    import sparse_kv_long_amd as se
+    from synth import make_snapkv_inputs
+
+    dev = "cuda"
+    t0 = time.time()
+    x = make_snapkv_inputs(wl, dev)
+    torch.cuda.synchronize()
+    gen_s = time.time() - t0
+    B, Hq, H, D, W, n, S = wl.batch, wl.num_q_heads, wl.num_kv_heads, wl.head_dim, wl.window, wl.prompt, wl.decode_steps
+    budgets = se.se_pyramid_budgets(wl.layers, wl.budget, *wl.layer_ratios)
+    layers = []
+    for R in budgets:
+        p = se.snapkv_params(B, Hq, H, D, n, W, wl.pool_kernel, max(R, 1), 1 << 30, wl.scale, sink=wl.sink,
+                             recent=wl.recent)
+        kcap = se.se_snapkv_kept_capacity(p)
+        C = (kcap + S + 15) // 16 * 16
+        p.out_capacity = C
+        st = {"p": p, "R": R, "C": C,
+              "ws": torch.empty(se.se_snapkv_workspace_size(p), dtype=torch.uint8, device=dev),
+              "k_out": torch.zeros((B, H, C, D), dtype=torch.bfloat16, device=dev),
+              "v_out": torch.zeros((B, H, C, D), dtype=torch.bfloat16, device=dev),
+              "kept": torch.empty((B, H, kcap), dtype=torch.int32, device=dev),
+              "klen": torch.empty((B, H), dtype=torch.int32, device=dev)}
+        se.se_snapkv_compact(p, x["q_win"], x["k"], x["v"], x["prompt_lens"], st["k_out"], st["v_out"], st["kept"],
+                             st["klen"], st["ws"])
+        torch.cuda.synchronize()
+        kl = int(st["klen"][0, 0])
+        assert (st["klen"] == kl).all()
+        st["kl"] = kl
+        st["k_out"][:, :, kl:kl + S] = x["k_steps"].permute(1, 2, 0, 3)
+        st["v_out"][:, :, kl:kl + S] = x["v_steps"].permute(1, 2, 0, 3)
+        MP = C // 16
+        st["pt"] = (torch.arange(B, device=dev)[:, None] * (H * MP) + torch.arange(MP, device=dev)[None]).to(torch.int32)
+        st["Ld"] = se.dense_layout(H, C, D)
+        st["Pd"] = se.decode_params(B, Hq, MP, MP, wl.scale)
+        st["wsd"] = torch.empty(se.se_sparse_decode_workspace_size(st["Ld"], st["Pd"]), dtype=torch.uint8, device=dev)
+        st["lens"] = [torch.full((B,), kl + s + 1, dtype=torch.int32, device=dev) for s in range(S)]
+        layers.append(st)
+    out = torch.empty((S, B, Hq, D), dtype=torch.float32, device=dev)
+    flush = make_flush(torch, not args.no_flush)
+
+    def evict_all(i):
+        for st in layers:
+            se.se_snapkv_compact(st["p"], x["q_win"], x["k"], x["v"], x["prompt_lens"], st["k_out"], st["v_out"],
+                                 st["kept"], st["klen"], st["ws"])
+
+    def decode_all(i):
+        # step s runs through every layer before step s + 1 (the model's order)
+        for s in range(S):
+            for st in layers:
+                se.se_sparse_decode(st["Ld"], st["Pd"], x["q_steps"][s], st["k_out"], st["v_out"], st["pt"], None,
+                                    st["lens"][s], out[s], None, st["wsd"])
+
+    decode_all(0)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        decode_all(0)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        decode_all(0)
+    out.zero_()
+    graph.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out, eager), "graph replay differs from the eager decode steps"
+
+    def whole(i):
+        evict_all(i)
+        graph.replay()
+
+    steps = max(1, args.steps // 10)
+    whole_ms, wall = timed_calls(whole, steps, 1, flush)
+    ev_ms, _ = timed_calls(evict_all, steps, 1, flush)
+    dec_ms, _ = timed_calls(lambda i: graph.replay(), steps, 1, None)
+    t_whole = float(np.mean(whole_ms)) * 1e-3
+    t_ev = float(np.mean(ev_ms)) * 1e-3
+    t_dec = float(np.mean(dec_ms)) * 1e-3
+    kls = [st["kl"] for st in layers]
+    b_evict = sum(B * Hq * W * D * 2 + B * H * n * D * 2 + 2 * 2 * B * H * kl * D * 2 + B * H * kl * 4 for kl in kls)
+    b_dec = sum(B * H * sum(kl + s + 1 for s in range(S)) * 2 * D * 2 + S * (B * Hq * D * 2 + B * Hq * D * 4)
+                for kl in kls)
+    result = {
+        "metric": f"PyramidKV eviction + decode tokens/s through a {wl.layers}-layer slice, 32K prompt, 1 GPU",
+        "value": round(B * S / t_whole, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": 1,
+        "ms_per_step": round(t_whole * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "method": wl.method, "layers": wl.layers,
+                   "layer_ratios": list(wl.layer_ratios), "layer_budgets": budgets, "kept_tokens": kls,
+                   "batch": B, "prompt": n, "num_q_heads": Hq, "num_kv_heads": H, "head_dim": D, "window": W,
+                   "pool_kernel": wl.pool_kernel, "sink": wl.sink, "recent": wl.recent, "decode_steps": S},
+        "effective_hbm_gbps": round((b_evict + b_dec) / t_whole / 1e9, 1),
+        "algorithmic_bytes_per_step": b_evict + b_dec,
+        "pieces_ms": {"evictions_all_layers": round(t_ev * 1e3, 4),
+                      "decode_steps_all_layers": round(t_dec * 1e3, 4)},
+        "eviction_gbps": round(b_evict / t_ev / 1e9, 1),
+        "decode_gbps_cache_resident": round(b_dec / t_dec / 1e9, 1),
+        "roofline": {"kernel": "decode over the layers' retained caches (split-K + merge)", "bound": "hbm",
+                     "achieved": round(b_dec / t_dec / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(b_dec / t_dec / 1e9 / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(b_dec / (S * len(layers)))},
+        "cache_flush_before_evictions": flush is not None,
+        "decode_steps_as_hip_graph": True,
+        "wall_s_timed_loop_incl_flush": round(wall, 4),
+        "input_generation_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_snapkv(wl, x, args.cpu_seconds, budgets)
+    print(json.dumps(result))
+
+
+def cpu_baseline_snapkv(wl, x, seconds, budgets=None):
     """The oracle's eviction (votes, pool, keep, row copies) and its decode
     steps over the kept rows, per (request, KV head) unit on one thread, until
     about `seconds` of CPU time are spent; scaled to the batch."""
@@ -458,12 +592,14 @@ def cpu_baseline_snapkv(wl, x, seconds):
     import oracle
     from synth import bf16_bits
 
-    G, W, R, S, n = wl.group, wl.window, wl.budget, wl.decode_steps, wl.prompt
-    units = [(b, g) for b in range(wl.batch) for g in range(wl.num_kv_heads)]
+    G, W, S, n = wl.group, wl.window, wl.decode_steps, wl.prompt
+    budgets = budgets or [wl.budget]
+    # (layer, request, KV head) units; one layer unless the workload has several
+    units = [(R, b, g) for R in budgets for b in range(wl.batch) for g in range(wl.num_kv_heads)]
     order = np.random.default_rng(0).permutation(len(units))
     spent, done = 0.0, 0
     while spent < seconds and done < len(units):
-        b, g = units[int(order[done])]
+        R, b, g = units[int(order[done])]
         qw = bf16_bits(x["q_win"][b, g * G:(g + 1) * G])
         kb, vb = bf16_bits(x["k"][b, g]), bf16_bits(x["v"][b, g])
         qs = bf16_bits(x["q_steps"][:, b, g * G:(g + 1) * G])
@@ -480,8 +616,9 @@ def cpu_baseline_snapkv(wl, x, seconds):
             spent += time.perf_counter() - t0
         done += 1
     step_s = spent / done * len(units)
+    what = "(layer, request, KV head)" if len(budgets) > 1 else "(request, KV head)"
     return {"value": round(wl.batch * S / step_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {len(units)} (request, KV head) units: fp64 numpy on one thread, votes over the "
+            "sample": f"{done} of {len(units)} {what} units: fp64 numpy on one thread, votes over the "
                       f"32K prompt, pool, keep, row copies and {S} decode steps each; {spent:.1f} s measured, "
                       f"scaled by units to the batch"}
 

@@ -87,6 +87,8 @@ class SnapKVWorkload:
     sink: int = 0                 # leading tokens always kept
     recent: int = 0               # trailing tokens always kept (at least the window)
     interval: tuple = (0, 0)      # history span that may be pruned; (0, 0): the whole prompt
+    layers: int = 1               # layers evicted per prefill (PyramidKV: one budget per layer)
+    layer_ratios: tuple = (1.0, 1.0)  # PyramidKV's first and last layer ratios
 
     @property
     def group(self) -> int:
@@ -121,11 +123,16 @@ H2O_32K = SnapKVWorkload("h2o_gqa32x8_d128_32k_b16", 16, 32, 8, 128, 32768, 128,
                          method="H2O", recent=4096)
 PRUNE_32K = SnapKVWorkload("prune_gqa32x8_d128_32k_b16", 16, 32, 8, 128, 32768, 32, 7, 2048, 64, seed=1004,
                            method="prefix-cache pruning", interval=(4096, 28672))
+# PyramidKV with Table 8's settings (sink 64, recent 512, 4,096 selected on
+# average, layer ratios 0.6 to 0.01, 32-token window; pooling 7 as SnapKV) over
+# a 4-layer slice of the stack; every layer sees the same synthetic cache.
+PYRAMID_32K = SnapKVWorkload("pyramid4_gqa32x8_d128_32k_b16", 16, 32, 8, 128, 32768, 32, 7, 4096, 64, seed=1004,
+                             method="PyramidKV", sink=64, recent=512, layers=4, layer_ratios=(0.6, 0.01))
 MLA_RAGGED = QuestWorkload("mla576_h32_ragged16k-128k_b16", 16, 32, 1, 576, 512, 131072, 256, "none",
                            v_is_k_prefix=True, ragged_lo=16384, seed=1005)
 
 WORKLOADS = {w.name: w for w in (TINY_QUEST, QWEN3_4B_32K, QWEN3_30B_128K, SNAPKV_32K, MLA_RAGGED, H2O_32K,
-                                 PRUNE_32K)}
+                                 PRUNE_32K, PYRAMID_32K)}
 
 
 def _gen(device, seed: int, tag: int) -> torch.Generator:

@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import sparse_kv_long_amd as se
-from synth import (H2O_32K, MLA_RAGGED, PRUNE_32K, QWEN3_4B_32K, QWEN3_30B_128K, SNAPKV_32K, make_quest_inputs,
+from synth import (H2O_32K, MLA_RAGGED, PRUNE_32K, PYRAMID_32K, QWEN3_4B_32K, QWEN3_30B_128K, SNAPKV_32K, make_quest_inputs,
                    make_snapkv_inputs, bf16_bits)
 from gpu_util import DEV, announce, build_summaries, check_attention, check_selection, layout_for, to_np, workspace
 
@@ -148,11 +148,18 @@ def test_snapkv_full_size_sampled_units():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("wl", [H2O_32K, PRUNE_32K], ids=lambda w: w.name)
-def test_eviction_family_full_size_sampled_units(wl):
-    """The H2O and prefix-pruning legs at the size the bench runs: counts,
-    forced tokens and bitwise copies on every unit, votes and selection on
-    sampled units against the oracle."""
+@pytest.mark.parametrize("name", ["h2o", "prune", "pyramid_layer0", "pyramid_layer3"])
+def test_eviction_family_full_size_sampled_units(name):
+    """The H2O, prefix-pruning and PyramidKV legs at the size the bench runs
+    (PyramidKV: its first and last layers' budgets): counts, forced tokens
+    and bitwise copies on every unit, votes and selection on sampled units
+    against the oracle."""
+    if name.startswith("pyramid"):
+        budgets = se.se_pyramid_budgets(PYRAMID_32K.layers, PYRAMID_32K.budget, *PYRAMID_32K.layer_ratios)
+        assert budgets == oracle.pyramid_budgets(PYRAMID_32K.layers, PYRAMID_32K.budget, *PYRAMID_32K.layer_ratios)
+        wl = PYRAMID_32K.resized(budget=budgets[int(name[-1])], layers=1)
+    else:
+        wl = {"h2o": H2O_32K, "prune": PRUNE_32K}[name]
     announce(f"full-size eviction {wl.name} seed {wl.seed}")
     x = make_snapkv_inputs(wl, DEV, with_decode=False)
     iv = wl.interval if wl.interval[1] else None

@@ -322,12 +322,13 @@ __device__ __forceinline__ uint32_t dword(const uint4& v, int i) {
 
 template <int G>
 struct MfmaDecodeShape {
-  static constexpr int PPS = G <= 8 ? 64 : 32;  // max pages per split
+  static constexpr int PPS = G <= 8 ? 256 : 128;  // max pages per split (ids staged in LDS)
 };
 
-// One block of 4 waves per (split, KV head, request); wave w streams pages
-// w, w+4, ... of the split with an online softmax, keeping the K and V
-// loads of the next two pages in flight.  Lane l = 16*kq + col.
+// One block of NW waves per (split, KV head, request); wave w streams pages
+// w, w+NW, ... of the split with an online softmax, keeping the K and V
+// loads of the next two pages in flight.  Lane l = 16*kq + col.  FINAL (one
+// split): the block normalises and writes the output itself, no merge.
 //   q.k   A = K (lane: token col, channels 8kq + 32ks), B = q (head col);
 //         output lane (col, kq): tokens 4kq + i of the page, head col.
 //   p.v   A = P (lane: head col, k 8kq + j = hi (j < 4) / lo (j >= 4) of
@@ -335,11 +336,12 @@ struct MfmaDecodeShape {
 //         -- the weights stay in the lanes that computed them, and the value
 //         rows are loaded whole (16 lanes per 256-byte row) and repacked
 //         in-lane with v_perm_b32.
-template <int G>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts,
-                                                         int pps, float scale2) {
-  constexpr int D = 128, NW = 4, PPS = MfmaDecodeShape<G>::PPS;
+template <int G, int NW, bool FINAL>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs,
+                                                              int64_t ts, int pps, float scale2) {
+  constexpr int D = 128, PPS = MfmaDecodeShape<G>::PPS;
   static_assert(G <= 16, "one 16-row head tile");
+  __shared__ float head_ml[16][2];  // FINAL: per head, the max and the weight sum over the waves
   __shared__ float comb[NW * G * D];
   __shared__ float wml[NW][G][2];
   __shared__ float alpha_lds[NW][16];
@@ -363,6 +365,10 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
   const int nsplit = gridDim.x;
   const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
   if (npg == 0) {
+    if (FINAL) {  // an empty request: a zero output row
+      for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) a.out[head0 * D + idx] = 0.f;
+      return;
+    }
     for (int h = threadIdx.x; h < G; h += blockDim.x) {
       a.part_ml[((head0 + h) * nsplit + split) * 2] = -__builtin_inff();
       a.part_ml[((head0 + h) * nsplit + split) * 2 + 1] = 0.f;
@@ -525,6 +531,35 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeArgs a, int Hkv,
     }
   }
   __syncthreads();
+  if (FINAL) {
+    if (threadIdx.x < G) {
+      const int h = threadIdx.x;
+      float M = -__builtin_inff();
+#pragma unroll
+      for (int q = 0; q < NW; ++q) M = fmaxf(M, wml[q][h][0]);
+      float L = 0.f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        const float mq = wml[q][h][0];
+        L += mq == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mq - M) * wml[q][h][1];
+      }
+      head_ml[h][0] = M;
+      head_ml[h][1] = L > 0.f ? 1.f / L : 0.f;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+      const int h = idx / D, c = idx % D;
+      const float M = head_ml[h][0];
+      float sacc = 0.f;
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        const float mq = wml[q][h][0];
+        sacc += mq == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(mq - M) * comb[(q * G + h) * D + c];
+      }
+      a.out[(head0 + h) * D + c] = sacc * head_ml[h][1];
+    }
+    return;
+  }
   const int64_t sbase = (int64_t)split;
   for (int idx = threadIdx.x; idx < G * (D + 2); idx += blockDim.x) {
     const int h = idx / (D + 2), c = idx % (D + 2);
@@ -957,7 +992,7 @@ static bool mla_decode_shape(const Layout& L, int G) {
 }
 
 static int max_pps(const Layout& L, int G) {
-  if (mfma_decode_shape(L, G)) return G <= 8 ? 64 : 32;
+  if (mfma_decode_shape(L, G)) return G <= 8 ? 256 : 128;
   if (mla_decode_shape(L, G)) return kMlaPagesPerSplit;
   return (L.dk <= 128 && G <= 16) ? 32 : 16;
 }
@@ -969,12 +1004,15 @@ int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, 
   const int units = B * L.hkv;
   const int mp = max_pps(L, Hq / L.hkv);
   const int smin = (kmax + mp - 1) / mp;
-  // about one full round of resident blocks (256 CUs x 2 blocks of the
-  // matrix-core kernel, x 4 of the VALU kernel): more splits only add per-block
-  // latency and merge traffic (measured), a partial second round idles the chip
+  // about one block per CU for the matrix-core GQA decode (measured at 128K,
+  // 256 kept pages: 2 splits = 256 blocks 54.3 us with the merge, 4 splits =
+  // 512 blocks 57.0 us, 1 split = 128 blocks 55.6 us without a merge: half the
+  // CUs idle), one full round of resident blocks for the others (x 4 for the
+  // VALU kernel); more splits only add per-block latency and merge traffic, a
+  // partial second round idles the chip
   const int G = Hq / L.hkv;
   const int target = mla_decode_shape(L, G) ? kMlaTargetBlocks / ((G + kMlaHeadsPerBlock - 1) / kMlaHeadsPerBlock)
-                     : mfma_decode_shape(L, G) ? 512 : 1024;
+                     : mfma_decode_shape(L, G) ? 256 : 1024;
   int s = requested > 0 ? requested : (target + units - 1) / units;
   // the matrix-core GQA decode keeps at least 32 pages (8 per wave) per split
   // while that still gives every CU a block: fewer leave each block with more
@@ -1025,7 +1063,14 @@ template <int G>
 static hipError_t launch_mfma_g(const Layout& L, const DecodeArgs& a, int pps, hipStream_t st) {
   const float scale2 = a.scale * kLog2e;
   dim3 grid(a.splits, L.hkv, a.B);
-  hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, pps, scale2);
+  if (a.splits == 1) {
+    // one block per (KV head, request) writes the output itself: no merge
+    hipLaunchKernelGGL((decode_mfma_kernel<G, 4, true>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, pps,
+                       scale2);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_mfma_kernel<G, 4, false>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, pps,
+                     scale2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, st, a.part_acc, a.part_ml, a.out, a.splits, 128);

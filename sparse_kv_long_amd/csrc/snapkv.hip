@@ -37,6 +37,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kRowsPerGroup = 128;
+// Pass 1 keeps a row's reference maximum while a tile's weights stay below
+// 2^20 in sum (so a row's sum stays far from the fp32 range over 32K keys).
+constexpr float kRowSlackSum = 1048576.0f;
 constexpr int kSnapWaves = 4;     // waves per block with one row group
 constexpr int kMaxRgWaves = 8;    // row groups a block can take as its waves
 
@@ -205,6 +208,19 @@ __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_rowstats_ke
       f32x16_t acc = {};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) acc = mfma32(kf[ks], qf[rt][ks], acc);
+      if (!edge) {
+        // the row's reference m stays put while the tile's weights 2^(z - m)
+        // sum to at most 2^kRowSlack: one fused multiply-add, exponential
+        // and add per key, no maximum (the first tile, where m = -inf, and a
+        // logit above m + kRowSlack take the exact step below)
+        float sf = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sf += __builtin_amdgcn_exp2f(fmaf(acc[r], scale2, -m[rt]));
+        if (sf <= kRowSlackSum) {
+          l[rt] += sf;
+          continue;
+        }
+      }
       float z[16];
       float tmax = -__builtin_inff();
 #pragma unroll

@@ -55,8 +55,7 @@ __global__ __launch_bounds__(256) void summary_build_kernel(const uint16_t* __re
     mn[e] = __builtin_inff();
     mx[e] = -__builtin_inff();
   }
-  for (int t = 0; t < valid; ++t) {
-    const uint4 w = ld16(src + t * ts);
+  auto fold = [&](const uint4& w) {
     const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -65,6 +64,17 @@ __global__ __launch_bounds__(256) void summary_build_kernel(const uint16_t* __re
       mn[2 * e + 1] = fminf(mn[2 * e + 1], bf_hi(d[e]));
       mx[2 * e + 1] = fmaxf(mx[2 * e + 1], bf_hi(d[e]));
     }
+  };
+  if (valid == kPage) {
+    // a full page: all 16 rows requested at once (a loop with a run-time
+    // count waited for each row in turn)
+    uint4 w[kPage];
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) w[t] = ldnt16(src + t * ts);
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) fold(w[t]);
+  } else {
+    for (int t = 0; t < valid; ++t) fold(ld16(src + t * ts));
   }
   uint32_t omn[4], omx[4];
 #pragma unroll
@@ -122,8 +132,7 @@ __device__ __forceinline__ void minmax8(const uint16_t* src, int64_t ts, int val
     mn[e] = __builtin_inff();
     mx[e] = -__builtin_inff();
   }
-  for (int t = 0; t < valid; ++t) {
-    const uint4 w = ld16(src + t * ts);
+  auto fold = [&](const uint4& w) {
     const uint32_t d[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -132,6 +141,17 @@ __device__ __forceinline__ void minmax8(const uint16_t* src, int64_t ts, int val
       mn[2 * e + 1] = fminf(mn[2 * e + 1], bf_hi(d[e]));
       mx[2 * e + 1] = fmaxf(mx[2 * e + 1], bf_hi(d[e]));
     }
+  };
+  if (valid == kPage) {
+    // a full page: all 16 rows requested at once (a loop with a run-time
+    // count waited for each row in turn)
+    uint4 w[kPage];
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) w[t] = ldnt16(src + t * ts);
+#pragma unroll
+    for (int t = 0; t < kPage; ++t) fold(w[t]);
+  } else {
+    for (int t = 0; t < valid; ++t) fold(ld16(src + t * ts));
   }
   omn = make_uint4(pack_bf16(mn[0], mn[1]), pack_bf16(mn[2], mn[3]), pack_bf16(mn[4], mn[5]), pack_bf16(mn[6], mn[7]));
   omx = make_uint4(pack_bf16(mx[0], mx[1]), pack_bf16(mx[2], mx[3]), pack_bf16(mx[4], mx[5]), pack_bf16(mx[6], mx[7]));

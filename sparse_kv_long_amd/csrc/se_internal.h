@@ -79,7 +79,6 @@ __host__ __device__ inline void snap_candidates(const SnapArgs& a, int n, int& l
 }
 struct SnapWork {
   float* row_part;  // [B, Hkv, row_groups, nblk*waves, 128, 2] partial (max, sum)
-  float* row_c;     // [B, Hq, W]   log2-domain normaliser per window row
   float* votes;     // [row_groups, B, Hkv, N]
   float* pooled;    // [B, Hkv, N]
 };

@@ -14,7 +14,7 @@
 // Two passes over the keys:
 //   pass 1 (rows x keys, keys as the MFMA M side): each lane holds one row and
 //          16 keys of a tile, so the running max and sum of 2^z per row are
-//          lane-local; partials per wave are merged by a small kernel into
+//          lane-local; pass 2's blocks merge each row's partials into
 //          c_r = max_r + log2(sum_r), the row's log2 normaliser.
 //   pass 2 (rows as the M side): each lane holds one key and 16 rows, so the
 //          vote 2^(z - c_r) summed over rows is lane-local.  Only prefix keys
@@ -111,7 +111,6 @@ size_t snap_workspace_bytes(const SnapArgs& a) {
   const SnapGeom s = snap_geom(a);
   size_t bytes = 0;
   bytes += align256((size_t)a.B * a.Hkv * s.nrg * s.slots * kRowsPerGroup * 2 * sizeof(float));
-  bytes += align256((size_t)a.B * a.Hq * a.W * sizeof(float));
   bytes += align256((size_t)s.nrg * a.B * a.Hkv * a.N * sizeof(float));
   bytes += align256((size_t)a.B * a.Hkv * a.N * sizeof(float));
   return bytes;
@@ -123,8 +122,6 @@ SnapWork snap_workspace_carve(const SnapArgs& a, void* ws) {
   SnapWork w;
   w.row_part = reinterpret_cast<float*>(p);
   p += align256((size_t)a.B * a.Hkv * s.nrg * s.slots * kRowsPerGroup * 2 * sizeof(float));
-  w.row_c = reinterpret_cast<float*>(p);
-  p += align256((size_t)a.B * a.Hq * a.W * sizeof(float));
   w.votes = reinterpret_cast<float*>(p);
   p += align256((size_t)s.nrg * a.B * a.Hkv * a.N * sizeof(float));
   w.pooled = reinterpret_cast<float*>(p);
@@ -259,30 +256,29 @@ __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_rowstats_ke
   // row tiles past NRT*32 inside the group do not exist; nothing else to write
 }
 
-// Merge the row-stat partials: c = max + log2(sum).  Grid (Hkv, B), 128 threads.
-__global__ __launch_bounds__(128) void snap_rowmerge_kernel(SnapArgs a, const float* __restrict__ row_part,
-                                                            float* __restrict__ row_c, int nrg, int slots, int skip_kept) {
-  const int b = blockIdx.y, g = blockIdx.x;
-  const int n = a.lens[b];
-  const int L = n - a.W;
-  if (L <= 0 || (skip_kept && nothing_dropped(a, n))) return;
-  const int G = a.Hq / a.Hkv;
-  const int rows = G * a.W;
-  for (int r = threadIdx.x; r < rows; r += blockDim.x) {
-    const int rg = r / kRowsPerGroup, rr = r % kRowsPerGroup;
-    const float* src = row_part + ((((int64_t)b * a.Hkv + g) * nrg + rg) * slots) * kRowsPerGroup * 2;
-    float M = -__builtin_inff();
-    for (int s = 0; s < slots; ++s) M = fmaxf(M, src[((int64_t)s * kRowsPerGroup + rr) * 2]);
-    // loads unconditional (a load under a branch waits before the next one issues)
-    float S = 0.f;
-    for (int s = 0; s < slots; ++s) {
-      const float ms = src[((int64_t)s * kRowsPerGroup + rr) * 2];
-      const float ls = src[((int64_t)s * kRowsPerGroup + rr) * 2 + 1];
-      S += ms == -__builtin_inff() ? 0.f : ls * __builtin_amdgcn_exp2f(ms - M);
-    }
-    const int hh = r / a.W, i = r % a.W;
-    row_c[((int64_t)b * a.Hq + g * G + hh) * a.W + i] = M + __builtin_amdgcn_logf(S);
+// A row's log2 normaliser c = max + log2(sum) from its pass-1 partials (one
+// (max, sum) pair per key-tile walker), eight pairs per memory round trip
+// (clamped indices keep the loads unconditional; repeats are not counted).
+__device__ __forceinline__ float row_normaliser(const float* __restrict__ row_part, const SnapArgs& a, int b, int g,
+                                                int rg, int rr, int nrg, int slots) {
+  const float* src = row_part + ((((int64_t)b * a.Hkv + g) * nrg + rg) * slots) * kRowsPerGroup * 2;
+  float M = -__builtin_inff(), S = 0.f;
+  for (int s0 = 0; s0 < slots; s0 += 8) {
+    float2 ml[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      ml[j] = *reinterpret_cast<const float2*>(src + ((int64_t)min(s0 + j, slots - 1) * kRowsPerGroup + rr) * 2);
+    float Mn = M;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) Mn = fmaxf(Mn, ml[j].x);
+    if (Mn == -__builtin_inff()) continue;  // no key seen yet
+    S = M == -__builtin_inff() ? 0.f : S * __builtin_amdgcn_exp2f(M - Mn);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      S += (s0 + j < slots && ml[j].x != -__builtin_inff()) ? ml[j].y * __builtin_amdgcn_exp2f(ml[j].x - Mn) : 0.f;
+    M = Mn;
   }
+  return M + __builtin_amdgcn_logf(S);
 }
 
 // ---------------------------------------------------------------------------
@@ -291,7 +287,7 @@ __global__ __launch_bounds__(128) void snap_rowmerge_kernel(SnapArgs a, const fl
 // ---------------------------------------------------------------------------
 template <int D, int NRT, bool RGW>
 __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_votes_kernel(SnapArgs a,
-                                                                                 const float* __restrict__ row_c,
+                                                                                 const float* __restrict__ row_part,
                                                                                  float* __restrict__ votes, int nrg,
                                                                                  int slots, int skip_kept,
                                                                                  float scale2) {
@@ -310,13 +306,15 @@ __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_votes_kerne
   // the candidates plus the pooling halo
   int vlo = 0, vhi = L;
   if (skip_kept) vote_span(a, n, vlo, vhi);
-  // normalisers of the block's row groups: all nrg with RGW, else its one
+  // normalisers of the block's row groups (all nrg with RGW, else its one),
+  // merged here from pass 1's partials (every block of the unit repeats this
+  // small merge instead of a kernel of its own)
   const int rg0 = RGW ? 0 : rg, nrg_blk = RGW ? nrg : 1;
   for (int r = threadIdx.x; r < nrg_blk * kRowsPerGroup; r += blockDim.x) {
-    const int gr = (rg0 + r / kRowsPerGroup) * kRowsPerGroup + r % kRowsPerGroup;
+    const int lrg = r / kRowsPerGroup, rr = r % kRowsPerGroup;
+    const int gr = (rg0 + lrg) * kRowsPerGroup + rr;
     // rows past G*W get +inf so their weight 2^(z - c) is 0
-    c_lds[r / kRowsPerGroup][r % kRowsPerGroup] =
-        gr < rows ? row_c[((int64_t)b * a.Hq + g * G + gr / a.W) * a.W + gr % a.W] : __builtin_inff();
+    c_lds[lrg][rr] = gr < rows ? row_normaliser(row_part, a, b, g, rg0 + lrg, rr, nrg, slots) : __builtin_inff();
   }
   __syncthreads();
   const float* cw = c_lds[RGW ? rg : 0];
@@ -364,12 +362,8 @@ static hipError_t launch_votes_t(const SnapArgs& a, const SnapWork& w, const Sna
                      scale2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(snap_rowmerge_kernel, dim3(a.Hkv, a.B), dim3(128), 0, st, a, w.row_part, w.row_c, s.nrg, s.slots,
-                     skip);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((snap_votes_kernel<D, NRT, RGW>), grid, block, 0, st, a, w.row_c, votes, s.nrg, s.slots, skip,
-                     scale2);
+  hipLaunchKernelGGL((snap_votes_kernel<D, NRT, RGW>), grid, block, 0, st, a, w.row_part, votes, s.nrg, s.slots,
+                     skip, scale2);
   return hipGetLastError();
 }
 

@@ -387,17 +387,21 @@ hipError_t launch_snap_votes(const SnapArgs& a, const SnapWork& w, bool skip_kep
 
 // ---------------------------------------------------------------------------
 // Max-pool of the votes (summed over row groups).  A block of 256 threads
-// pools 256 positions: it sums the row groups of its positions plus a halo of
-// `radius` on each side once into LDS, then every thread takes the max over
-// its window from LDS.
+// pools 2048 positions, eight per thread (256 apart): it sums the row
+// groups of its positions plus a halo of `radius` on each side once into LDS
+// (every load of the staging issued before the first is used), then every
+// thread takes the max over its positions' windows from LDS.
 // ---------------------------------------------------------------------------
-constexpr int kPoolTile = 256;
+constexpr int kPoolThreads = 256;
+constexpr int kPoolPerThread = 8;
+constexpr int kPoolTile = kPoolThreads * kPoolPerThread;
 constexpr int kPoolMaxRadius = kMaxPoolKernel / 2;
+constexpr int kPoolStage = (kPoolTile + 2 * kPoolMaxRadius + kPoolThreads - 1) / kPoolThreads;  // loads per thread
 
-__global__ __launch_bounds__(kPoolTile) void maxpool_kernel(SnapArgs a, const float* __restrict__ votes,
-                                                            float* __restrict__ pooled, int radius, int nrg,
-                                                            int skip_kept) {
-  __shared__ float sv[kPoolTile + 2 * kPoolMaxRadius];
+__global__ __launch_bounds__(kPoolThreads) void maxpool_kernel(SnapArgs a, const float* __restrict__ votes,
+                                                               float* __restrict__ pooled, int radius, int nrg,
+                                                               int skip_kept) {
+  __shared__ float sv[kPoolStage * kPoolThreads];
   const int j0 = blockIdx.x * kPoolTile;
   const int g = blockIdx.y, b = blockIdx.z;
   const int B = a.B, Hkv = a.Hkv, N = a.N;
@@ -412,21 +416,30 @@ __global__ __launch_bounds__(kPoolTile) void maxpool_kernel(SnapArgs a, const fl
     vote_span(a, n, vlo, vhi);
   }
   if (j0 >= hi || j0 + kPoolTile <= lo) return;
-  for (int i = threadIdx.x; i < kPoolTile + 2 * radius; i += kPoolTile) {
+  const int span = kPoolTile + 2 * radius;
+  float v[kPoolStage];
+#pragma unroll
+  for (int u = 0; u < kPoolStage; ++u) {
+    const int i = u * kPoolThreads + threadIdx.x;
     const int t = j0 - radius + i;
-    float v = -__builtin_inff();
-    if (t >= vlo && t < vhi) {
-      v = 0.f;
-      for (int rg = 0; rg < nrg; ++rg) v += votes[(((int64_t)rg * B + b) * Hkv + g) * N + t];
-    }
-    sv[i] = v;
+    const bool in = i < span && t >= vlo && t < vhi;
+    const int tc = in ? t : vlo;  // clamped: the load is issued either way, its value dropped
+    float x = 0.f;
+    for (int rg = 0; rg < nrg; ++rg) x += votes[(((int64_t)rg * B + b) * Hkv + g) * N + tc];
+    v[u] = in ? x : -__builtin_inff();
   }
+#pragma unroll
+  for (int u = 0; u < kPoolStage; ++u) sv[u * kPoolThreads + threadIdx.x] = v[u];
   __syncthreads();
-  const int j = j0 + threadIdx.x;
-  if (j < lo || j >= hi) return;
-  float best = -__builtin_inff();
-  for (int d = 0; d <= 2 * radius; ++d) best = fmaxf(best, sv[threadIdx.x + d]);
-  pooled[((int64_t)b * Hkv + g) * N + j] = best;
+#pragma unroll
+  for (int e = 0; e < kPoolPerThread; ++e) {
+    const int j = j0 + e * kPoolThreads + threadIdx.x;  // consecutive lanes, consecutive positions
+    if (j < lo || j >= hi) continue;
+    float best = -__builtin_inff();
+    const float* w = sv + e * kPoolThreads + threadIdx.x;
+    for (int d = 0; d <= 2 * radius; ++d) best = fmaxf(best, w[d]);
+    pooled[((int64_t)b * Hkv + g) * N + j] = best;
+  }
 }
 
 hipError_t launch_maxpool(const SnapArgs& a, const float* votes, int row_groups, float* pooled, bool skip_kept,
@@ -434,7 +447,7 @@ hipError_t launch_maxpool(const SnapArgs& a, const float* votes, int row_groups,
   if (a.B == 0) return hipSuccess;
   if (a.pool / 2 > kPoolMaxRadius) return hipErrorInvalidValue;
   dim3 grid((a.N + kPoolTile - 1) / kPoolTile, a.Hkv, a.B);
-  hipLaunchKernelGGL(maxpool_kernel, grid, dim3(kPoolTile), 0, st, a, votes, pooled, a.pool / 2, row_groups,
+  hipLaunchKernelGGL(maxpool_kernel, grid, dim3(kPoolThreads), 0, st, a, votes, pooled, a.pool / 2, row_groups,
                      skip_kept ? 1 : 0);
   return hipGetLastError();
 }

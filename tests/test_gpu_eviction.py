@@ -220,3 +220,37 @@ def test_reeviction_after_decode_steps(first_interval):
     for b in range(B):
         ref = oracle.decode_over_rows(qs[b], ko2[b], vo2[b], int(dl[b]), G, wl.scale)
         check_attention(o[b], ref, float(np.abs(oracle.bf16_to_f64(vo2[b])).max()), f"decode after re-evict b{b}")
+
+
+@pytest.mark.parametrize("sink,recent,interval", [(5, 40, None), (0, 0, (60, 250)), (30, 70, (10, 200)),
+                                                  (0, 120, None)])
+def test_select_and_compact_exact_on_given_votes(sink, recent, interval):
+    """se_maxpool1d, se_snapkv_select and se_compact one by one on integer-valued
+    votes (ties on purpose): the pooled values and the kept positions equal the
+    oracle's exactly (the lower position wins a tie), and the copies are bitwise."""
+    wl = SnapKVWorkload("e_sel", 3, 8, 2, 128, 300, 16, 5, 40, 0, seed=49)
+    lens = [300, 171, 90]
+    x = make_snapkv_inputs(wl, DEV, prompt_lens=lens, with_decode=False)
+    p, kcap = params(wl, sink, recent, interval)
+    rng = np.random.default_rng(49)
+    votes = rng.integers(0, 6, (wl.batch, wl.num_kv_heads, wl.prompt)).astype(np.float32) / 4
+    pooled = torch.full((wl.batch, wl.num_kv_heads, wl.prompt), float("nan"), device=DEV)
+    se.se_maxpool1d(p, torch.from_numpy(votes).to(DEV), x["prompt_lens"], pooled)
+    kept = torch.full((wl.batch, wl.num_kv_heads, kcap), 777, dtype=torch.int32, device=DEV)
+    klen = torch.zeros((wl.batch, wl.num_kv_heads), dtype=torch.int32, device=DEV)
+    se.se_snapkv_select(p, pooled, x["prompt_lens"], kept, klen)
+    k_out = torch.zeros((wl.batch, wl.num_kv_heads, p.out_capacity, wl.head_dim), dtype=torch.bfloat16, device=DEV)
+    v_out = torch.zeros_like(k_out)
+    se.se_compact(p, x["k"], x["v"], kept, klen, k_out, v_out)
+    torch.cuda.synchronize()
+    Pg, K, KL = to_np(pooled), to_np(kept), to_np(klen)
+    kb, vb, ko, vo = bf16_bits(x["k"]), bf16_bits(x["v"]), bf16_bits(k_out), bf16_bits(v_out)
+    for b, n in enumerate(lens):
+        L = n - wl.window
+        for g in range(wl.num_kv_heads):
+            want_pool = oracle.maxpool1d(votes[b, g, :L].astype(np.float64), wl.pool_kernel)
+            assert (Pg[b, g, :L] == want_pool).all()
+            keep = oracle.eviction_unit_keep(want_pool, n, wl.window, wl.budget, sink, recent, interval)
+            assert KL[b, g] == len(keep), (b, g)
+            assert (K[b, g, :len(keep)] == keep).all() and (K[b, g, len(keep):] == -1).all(), (b, g)
+            assert (ko[b, g, :len(keep)] == kb[b, g, keep]).all() and (vo[b, g, :len(keep)] == vb[b, g, keep]).all()

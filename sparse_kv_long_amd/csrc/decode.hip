@@ -897,9 +897,64 @@ constexpr int kMaxSplits = 1024;
 // Few splits (the common case): every thread loads all (m, l) pairs of its
 // (request, head) and four acc columns of every split at once, so the merge
 // takes one memory round trip and no barrier.  Indices past nsplit are
-// clamped and masked.
+// clamped and masked.  A 128-thread block takes 128 / (DV / 4) heads (four at
+// DV = 128), so that no thread idles.
 constexpr int kMergeFew = 16;
+constexpr int kMergeThreads = 128;
 
+template <int NS>
+__global__ __launch_bounds__(kMergeThreads) void merge_few_kernel(const float* __restrict__ part_acc,
+                                                                  const float* __restrict__ part_ml,
+                                                                  float* __restrict__ out, int nsplit, int DV,
+                                                                  int64_t nheads) {
+  const int tph = DV / 4;  // threads per head
+  const int hpb = tph < kMergeThreads ? kMergeThreads / tph : 1;
+  const int64_t bh = (int64_t)blockIdx.x * hpb + threadIdx.x / tph;
+  if (bh >= nheads) return;
+  const float* ml = part_ml + bh * nsplit * 2;
+  const float* acc = part_acc + bh * nsplit * DV;
+  for (int c = 4 * (threadIdx.x % tph); c < DV; c += 4 * (tph < kMergeThreads ? tph : kMergeThreads)) {
+    float m[NS], l[NS];
+    float4 v[NS];
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) {
+      const int s = min(sp, nsplit - 1);
+      m[sp] = ml[2 * s];
+      l[sp] = ml[2 * s + 1];
+      v[sp] = *reinterpret_cast<const float4*>(acc + (int64_t)s * DV + c);
+    }
+    float M = -__builtin_inff();
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) M = fmaxf(M, m[sp]);
+    float den = 0.f;
+    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int sp = 0; sp < NS; ++sp) {
+      // an empty split (m = -inf) never wrote its acc; a clamped duplicate
+      // (sp >= nsplit) is not counted
+      const bool live = sp < nsplit && m[sp] != -__builtin_inff();
+      const float wgt = live ? __builtin_amdgcn_exp2f(m[sp] - M) : 0.f;
+      den += wgt * l[sp];
+      num.x += live ? wgt * v[sp].x : 0.f;
+      num.y += live ? wgt * v[sp].y : 0.f;
+      num.z += live ? wgt * v[sp].z : 0.f;
+      num.w += live ? wgt * v[sp].w : 0.f;
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    float* o = out + bh * DV + c;
+    if ((reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+      *reinterpret_cast<float4*>(o) = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
+    } else {  // the output need only be 4-byte aligned
+      o[0] = num.x * inv;
+      o[1] = num.y * inv;
+      o[2] = num.z * inv;
+      o[3] = num.w * inv;
+    }
+  }
+}
+
+// Many splits: one block per (request, query head), weights through LDS as
+// described above.
 __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ part_acc,
                                                     const float* __restrict__ part_ml, float* __restrict__ out,
                                                     int nsplit, int DV) {
@@ -907,47 +962,6 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
   const int64_t bh = blockIdx.x;
   const float* ml = part_ml + bh * nsplit * 2;
   const float* acc = part_acc + bh * nsplit * DV;
-  if (nsplit <= kMergeFew) {
-    for (int c = 4 * threadIdx.x; c < DV; c += 4 * blockDim.x) {
-      float m[kMergeFew], l[kMergeFew];
-      float4 v[kMergeFew];
-#pragma unroll
-      for (int sp = 0; sp < kMergeFew; ++sp) {
-        const int s = min(sp, nsplit - 1);
-        m[sp] = ml[2 * s];
-        l[sp] = ml[2 * s + 1];
-        v[sp] = *reinterpret_cast<const float4*>(acc + (int64_t)s * DV + c);
-      }
-      float M = -__builtin_inff();
-#pragma unroll
-      for (int sp = 0; sp < kMergeFew; ++sp) M = fmaxf(M, m[sp]);
-      float den = 0.f;
-      float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int sp = 0; sp < kMergeFew; ++sp) {
-        // an empty split (m = -inf) never wrote its acc; a clamped duplicate
-        // (sp >= nsplit) is not counted
-        const bool live = sp < nsplit && m[sp] != -__builtin_inff();
-        const float wgt = live ? __builtin_amdgcn_exp2f(m[sp] - M) : 0.f;
-        den += wgt * l[sp];
-        num.x += live ? wgt * v[sp].x : 0.f;
-        num.y += live ? wgt * v[sp].y : 0.f;
-        num.z += live ? wgt * v[sp].z : 0.f;
-        num.w += live ? wgt * v[sp].w : 0.f;
-      }
-      const float inv = den > 0.f ? 1.f / den : 0.f;
-      float* o = out + bh * DV + c;
-      if ((reinterpret_cast<uintptr_t>(out) & 15) == 0) {
-        *reinterpret_cast<float4*>(o) = make_float4(num.x * inv, num.y * inv, num.z * inv, num.w * inv);
-      } else {  // the output need only be 4-byte aligned
-        o[0] = num.x * inv;
-        o[1] = num.y * inv;
-        o[2] = num.z * inv;
-        o[3] = num.w * inv;
-      }
-    }
-    return;
-  }
   if (threadIdx.x < kWave) {
     const int lane = threadIdx.x;
     float M = -__builtin_inff();
@@ -979,6 +993,29 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ pa
     for (; sp < nsplit; ++sp) num += term(sp, acc[(int64_t)sp * DV + c]);
     out[bh * DV + c] = num;
   }
+}
+
+// The split merge for DV channels per head: few splits pack several heads
+// into a block; many splits take the LDS path.
+static hipError_t launch_merge(const DecodeArgs& a, int DV, hipStream_t st) {
+  const int64_t nheads = (int64_t)a.B * a.Hq;
+  if (a.splits > kMergeFew) {
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)nheads), dim3(128), 0, st, a.part_acc, a.part_ml, a.out, a.splits,
+                       DV);
+    return hipGetLastError();
+  }
+  const int tph = DV / 4;
+  const int hpb = tph < kMergeThreads ? kMergeThreads / tph : 1;
+  const dim3 grid((unsigned)((nheads + hpb - 1) / hpb));
+#define SE_M(NS)                                                                                                   \
+  if (a.splits <= NS) {                                                                                            \
+    hipLaunchKernelGGL(merge_few_kernel<NS>, grid, dim3(kMergeThreads), 0, st, a.part_acc, a.part_ml, a.out,        \
+                       a.splits, DV, nheads);                                                                      \
+    return hipGetLastError();                                                                                      \
+  }
+  SE_M(2) SE_M(4) SE_M(8) SE_M(16)
+#undef SE_M
+  return hipErrorInvalidValue;
 }
 
 bool use_mfma_decode();
@@ -1042,8 +1079,7 @@ static hipError_t launch_g(const Layout& L, const DecodeArgs& a, int pps, hipStr
                      pps, scale2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, st, a.part_acc, a.part_ml, a.out, a.splits, DV);
-  return hipGetLastError();
+  return launch_merge(a, DV, st);
 }
 
 template <int DK, int DV, bool VISK>
@@ -1073,8 +1109,7 @@ static hipError_t launch_mfma_g(const Layout& L, const DecodeArgs& a, int pps, h
                      scale2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, st, a.part_acc, a.part_ml, a.out, a.splits, 128);
-  return hipGetLastError();
+  return launch_merge(a, 128, st);
 }
 
 static hipError_t launch_mla(const Layout& L, const DecodeArgs& a, int pps, hipStream_t st) {
@@ -1088,8 +1123,7 @@ static hipError_t launch_mla(const Layout& L, const DecodeArgs& a, int pps, hipS
                      nhb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(a.B * a.Hq), dim3(128), 0, st, a.part_acc, a.part_ml, a.out, a.splits, 512);
-  return hipGetLastError();
+  return launch_merge(a, 512, st);
 }
 
 // Decode path: the matrix-core kernels for Dk = Dv = 128 with G <= 16 and for

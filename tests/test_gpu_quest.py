@@ -275,12 +275,15 @@ def test_sink_and_recent_only_needs_no_summaries(name):
     check_attention(to_np(out), ref, vmax, f"{name} sink/recent only")
 
 
-def test_empty_and_single_token_requests():
+@pytest.mark.parametrize("splits", [0, 1, 2])
+def test_empty_and_single_token_requests(splits):
+    """Lengths 0, 1, 16 and 17 with the automatic split count, one split (the
+    decode writes the output itself, no merge) and two."""
     wl = QuestWorkload("t_edge", 4, 8, 2, 128, 128, 64, 2, "none", seed=21)
-    announce("edge lengths [0, 1, 16, 17]")
+    announce(f"edge lengths [0, 1, 16, 17], splits {splits}")
     x = make_quest_inputs(wl, DEV, poison_tail=True, seq_lens=[0, 1, 16, 17])
     summ = build_summaries(x, wl)
-    out, sel = run_sparse_decode(x, wl, summ)
+    out, sel = run_sparse_decode(x, wl, summ, splits=splits)
     o = to_np(out)
     assert (o[0] == 0).all()
     h = host_inputs(x)

@@ -296,7 +296,8 @@ int se_pyramid_budgets(int32_t num_layers, int32_t budget, double ratio_first, d
  * required; other entries are untouched.  se_snapkv_votes needs the same
  * workspace as se_snapkv_compact.  se_maxpool1d pools the whole prefix;
  * se_snapkv_select writes kept_idx [B, Hkv, kcap] of prompt positions and
- * se_compact copies the rows kept_idx names. */
+ * se_compact copies the rows kept_idx names (k_out/v_out must not overlap
+ * k/v: SE_EINVAL). */
 int se_snapkv_votes(const se_snapkv_params* params, const void* q_win, const void* k,
                     const int32_t* prompt_lens, float* votes, void* workspace, size_t workspace_bytes,
                     void* stream);

@@ -378,6 +378,16 @@ static bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// The compaction reads rows of k/v while it writes k_out/v_out, so the two
+// pairs must not share memory.
+static bool outputs_overlap_inputs(const se_snapkv_params* p, const void* k, const void* v, const void* k_out,
+                                   const void* v_out) {
+  const size_t in_bytes = (size_t)p->batch * p->num_kv_heads * p->max_prompt_len * p->head_dim * 2;
+  const size_t out_bytes = (size_t)p->batch * p->num_kv_heads * p->out_capacity * p->head_dim * 2;
+  return overlaps(k, in_bytes, k_out, out_bytes) || overlaps(k, in_bytes, v_out, out_bytes) ||
+         overlaps(v, in_bytes, k_out, out_bytes) || overlaps(v, in_bytes, v_out, out_bytes);
+}
+
 static int snap_evict(const se_snapkv_params* params, const void* q_win, const void* k, const void* v,
                       const int32_t* prompt_lens, const int32_t* positions, void* k_out, void* v_out,
                       int32_t* kept_idx, int32_t* kept_len, void* workspace, size_t workspace_bytes, void* stream) {
@@ -386,12 +396,7 @@ static int snap_evict(const se_snapkv_params* params, const void* q_win, const v
   if (params->batch == 0) return SE_OK;
   if (!q_win || !k || !v || !prompt_lens || !k_out || !v_out || !kept_idx || !kept_len) return SE_EINVAL;
   if (!aligned16(q_win) || !aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out)) return SE_EINVAL;
-  // the compaction reads rows of k/v while it writes k_out/v_out
-  const size_t in_bytes = (size_t)params->batch * params->num_kv_heads * params->max_prompt_len * params->head_dim * 2;
-  const size_t out_bytes = (size_t)params->batch * params->num_kv_heads * params->out_capacity * params->head_dim * 2;
-  if (overlaps(k, in_bytes, k_out, out_bytes) || overlaps(k, in_bytes, v_out, out_bytes) ||
-      overlaps(v, in_bytes, k_out, out_bytes) || overlaps(v, in_bytes, v_out, out_bytes))
-    return SE_EINVAL;
+  if (outputs_overlap_inputs(params, k, v, k_out, v_out)) return SE_EINVAL;
   const se::SnapArgs a = snap_args(params, q_win, k, v, prompt_lens);
   rc = check_ws(a, workspace, workspace_bytes);
   if (rc) return rc;
@@ -507,6 +512,7 @@ int se_compact(const se_snapkv_params* params, const void* k, const void* v, con
   if (params->batch == 0) return SE_OK;
   if (!k || !v || !kept_idx || !kept_len || !k_out || !v_out) return SE_EINVAL;
   if (!aligned16(k) || !aligned16(v) || !aligned16(k_out) || !aligned16(v_out)) return SE_EINVAL;
+  if (outputs_overlap_inputs(params, k, v, k_out, v_out)) return SE_EINVAL;
   const se::SnapArgs a = snap_args(params, nullptr, k, v, nullptr);
   return hip_status(se::launch_compact(a, kept_idx, kept_len, static_cast<uint16_t*>(k_out),
                                        static_cast<uint16_t*>(v_out), (hipStream_t)stream));

@@ -177,6 +177,7 @@ def test_snapkv_pointer_and_workspace_errors():
     assert se.lib().se_maxpool1d(ctypes.byref(p), None, FAKE, FAKE, None) == se.SE_EINVAL
     assert se.lib().se_snapkv_select(ctypes.byref(p), FAKE, None, FAKE, FAKE, None) == se.SE_EINVAL
     assert se.lib().se_compact(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, None) == se.SE_EINVAL
+    assert se.lib().se_compact(ctypes.byref(p), FAKE, OUT2, FAKE, FAKE, OUT1, OUT2 + 64, None) == se.SE_EINVAL
 
 
 def test_product_path_does_not_import_the_oracle():

@@ -145,18 +145,27 @@ def test_pyramid_layers_match_oracle():
                            f"layer {layer} b{b} g{g}")
 
 
-@pytest.mark.parametrize("first_interval", [None, (40, 600)])
-def test_reeviction_after_decode_steps(first_interval):
+# (window, pool, decode steps, sink, recent, budget of the second eviction, first interval)
+REEVICT = {
+    "snapkv": (16, 7, 48, 4, 32, 50, None),
+    "snapkv_interval": (16, 7, 48, 4, 32, 50, (40, 600)),
+    # H2O's shape: a 128-query window (four row groups), no pooling, the recent share as forced tokens
+    "h2o": (128, 1, 136, 0, 150, 90, None),
+}
+
+
+@pytest.mark.parametrize("case", sorted(REEVICT))
+def test_reeviction_after_decode_steps(case):
     """Prefill eviction, decode steps appended to the retained cache, then a
     second eviction over that cache with the last W decode queries as the
     window; kept_idx must report original positions, and a decode step over
     the re-evicted cache must match the oracle."""
-    wl = SnapKVWorkload("e_re", 3, 8, 2, 128, 900, 16, 7, 120, 48, seed=46)
+    W_, pool, steps, sink, recent, budget2, first_interval = REEVICT[case]
+    wl = SnapKVWorkload("e_re", 3, 8, 2, 128, 900, W_, pool, 120, steps, seed=46)
     lens = [900, 610, 300]
-    announce(f"re-eviction seed {wl.seed} lens {lens} first interval {first_interval}")
+    announce(f"re-eviction {case} seed {wl.seed} lens {lens}")
     x = make_snapkv_inputs(wl, DEV, prompt_lens=lens)
     B, H, D, G, S, W = wl.batch, wl.num_kv_heads, wl.head_dim, wl.group, wl.decode_steps, wl.window
-    sink, recent = 4, 32
     p1, kcap1 = params(wl, sink, recent, first_interval)
     C1 = -(-(kcap1 + S) // 16) * 16
     p1.out_capacity = C1
@@ -176,7 +185,7 @@ def test_reeviction_after_decode_steps(first_interval):
         kl = int(KL1[b, 0])
         positions[b, :, kl:kl + S] = torch.arange(lens[b], lens[b] + S, dtype=torch.int32, device=DEV)
     q_win2 = x["q_steps"][S - W:].permute(1, 2, 0, 3).contiguous()  # [B, Hq, W, D]
-    wl2 = wl.resized(budget=50)
+    wl2 = wl.resized(budget=budget2)
     p2, kcap2 = params(wl2, sink, recent, None, max_len=C1)
     k2, v2, kept2, klen2 = run_evict(p2, kcap2, q_win2, k1, v1, cache_lens, positions=positions)
 

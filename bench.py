@@ -436,11 +436,7 @@ def bench_snapkv(args, wl):
         "eviction_vote_columns_pass2": vcols,
         "eviction_gbps": round(b_evict / t_ev / 1e9, 1),
         "decode_gbps_cache_resident": round(b_dec / t_dec / 1e9, 1),
-        "roofline": {"kernel": "snapkv votes (row statistics + votes, MFMA)", "bound": "hbm",
-                     "achieved": round(b_votes / t_votes / 1e9, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(b_votes / t_votes / 1e9 / HBM_PEAK_GBPS, 4), "traffic": traffic_record("snapkv_votes", wl.name),
-                     "algorithmic_bytes_per_launch": b_votes,
-                     "mfma_tflops": round(flops_votes / t_votes / 1e12, 1), "mfma_peak_tflops": 2500.0},
+        "roofline": votes_roofline(b_votes, flops_votes, t_votes, traffic_record("snapkv_votes", wl.name)),
         "cache_flush_before_eviction": flush is not None,
         "decode_steps_as_hip_graph": True,
         "wall_s_timed_loop_incl_flush": round(wall, 4),
@@ -580,6 +576,30 @@ def bench_pyramid(args, wl):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_snapkv(wl, x, args.cpu_seconds, budgets)
     print(json.dumps(result))
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def votes_roofline(b_votes, flops_votes, t_votes, traffic):
+    """Roofline of the window x context scoring (row statistics + votes): the
+    bound is the one its arithmetic intensity puts it under -- HBM below the
+    bf16 ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B; SnapKV's 32-row window,
+    128 flop/B), the matrix cores above it (H2O's 128-row window, 512 flop/B)."""
+    intensity = flops_votes / b_votes
+    gbps = b_votes / t_votes / 1e9
+    tflops = flops_votes / t_votes / 1e12
+    ridge = MFMA_BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    r = {"kernel": "snapkv votes (row statistics + votes, MFMA)", "arithmetic_intensity_flop_per_byte":
+         round(intensity, 1), "traffic": traffic, "algorithmic_bytes_per_launch": b_votes,
+         "algorithmic_flops_per_launch": flops_votes, "hbm_gbps": round(gbps, 1), "mfma_tflops": round(tflops, 1)}
+    if intensity < ridge:
+        r.update({"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                  "frac": round(gbps / HBM_PEAK_GBPS, 4)})
+    else:
+        r.update({"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                  "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)})
+    return r
 
 
 def cpu_baseline_snapkv(wl, x, seconds, budgets=None):

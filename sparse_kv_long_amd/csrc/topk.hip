@@ -122,10 +122,22 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ row, int N,
 #pragma unroll
     for (int i = 0; i < KPT; ++i) key[i] = (base + i < N) ? float_key(row[base + i]) : 0u;
   }
-  // the translations are fetched with the keys, off the critical path
+  // the translations are fetched with the keys, off the critical path (16
+  // bytes per load where the run is whole and aligned)
   if (translate) {
+    if (KPT >= 4 && full && (((uintptr_t)translate) & 15) == 0) {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) tr[i] = (base + i < N) ? translate[base + i] : 0;
+      for (int i = 0; i < KPT; i += 4) {
+        const int4 t4 = *reinterpret_cast<const int4*>(translate + base + i);
+        tr[i] = t4.x;
+        tr[i + 1] = t4.y;
+        tr[i + 2] = t4.z;
+        tr[i + 3] = t4.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) tr[i] = (base + i < N) ? translate[base + i] : 0;
+    }
   }
 #pragma unroll
   for (int i = 0; i < KPT; ++i)

@@ -156,6 +156,8 @@ def main():
 
     # whole step
     step_ms, wall = timed(step, args.steps, args.warmup)
+    # the same step with warm caches (no flush), for information
+    hot_ms, _ = timed_calls(step, args.steps, 2, None)
     # per-step pieces, each timed alone on the same inputs
     def k1(i):
         se.se_quest_scores(L, P, qs[i % nq], x["k_pages"], x["page_table"], summ, x["seq_lens"], scores)
@@ -214,8 +216,10 @@ def main():
         "pct_peak_hbm": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_step": b_alg,
         "step_ms_p10_p50_p90": [round(float(np.percentile(step_ms, p)), 4) for p in (10, 50, 90)],
+        "step_ms_hot_p50": round(float(np.median(hot_ms)), 4),
         "wall_s_timed_loop_incl_flush": round(wall, 4),
         "cache_flush_between_steps": flush is not None,
+        **stream_read_reference(torch, gbps),
         "pieces_ms": {"quest_scores": round(float(np.mean(k1_ms)), 4), "topk_pages": round(float(np.mean(k2_ms)), 4),
                       "decode_and_merge": round(float(np.mean(k34_ms)), 4)},
         "roofline": roofline,
@@ -266,6 +270,37 @@ def timed_calls(fn, count, warm, flush):
     wall = time.perf_counter() - wall0
     ms = np.array([a.elapsed_time(b) for a, b in evs])
     return ms, wall
+
+
+def stream_read_reference(torch, gbps):
+    """The rate of a plain streaming read on this GPU (`se_hbm_read` from
+    libse_hbmread.so: 1 GiB read once, 16 B per lane per load; the best of a
+    few grid sizes, median of 10 event-timed calls each) and the step's
+    effective rate as a fraction of it."""
+    import ctypes
+    import numpy as np
+    from sparse_kv_long_amd.probe.build import PROBE_LIB
+    if not os.path.exists(PROBE_LIB):
+        raise RuntimeError(f"{PROBE_LIB} is missing: build it first (python -m sparse_kv_long_amd.probe.build)")
+    h = ctypes.CDLL(PROBE_LIB)
+    h.se_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    h.se_hbm_read.restype = ctypes.c_int
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros((1,), dtype=torch.int32, device="cuda")
+    best, best_blocks = 0.0, 0
+    for blocks in (1024, 4096, 16384, 65536):
+        def read(i):
+            rc = h.se_hbm_read(buf.data_ptr(), nbytes, blocks, sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"se_hbm_read failed: {rc}")
+        ms, _ = timed_calls(read, 10, 3, None)
+        rate = nbytes / (float(np.median(ms)) * 1e-3) / 1e9
+        if rate > best:
+            best, best_blocks = rate, blocks
+    del buf
+    return {"stream_read_gbps": round(best, 1), "frac_of_stream_read": round(gbps / best, 4),
+            "stream_read_kernel": f"se_hbm_read, 1 GiB, {best_blocks} blocks of 256 threads"}
 
 
 def make_flush(torch, enabled):

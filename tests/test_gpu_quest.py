@@ -322,3 +322,40 @@ def test_longest_supported_request():
     vals = oracle.unit_selected_tokens(vp, chosen, n)
     ref = oracle.unit_attention(qf, keys, vals, wl.scale)
     check_attention(to_np(out)[0], ref, float(np.abs(vals).max()), "1M")
+
+
+@pytest.mark.parametrize("name", ["d128_g8", "mla"])
+def test_shared_prefix_pages_match_oracle(name):
+    """Requests whose page tables point at the same physical pages for a
+    common prefix (a shared prompt): summaries stay per physical page and
+    bitwise, every request's selection and attention follow the oracle on the
+    same page table, and the refresh of each request's own last page leaves
+    the shared pages as built."""
+    base, _ = SMALL[name]
+    wl = QuestWorkload(base.name + "_shared", 3, base.num_q_heads, base.num_kv_heads, base.head_dim_qk,
+                       base.head_dim_v, base.context, base.topk, base.saliency, v_is_k_prefix=base.v_is_k_prefix,
+                       seed=base.seed + 100)
+    lens = [wl.context, wl.context - 37, wl.context - 300]
+    shared = 30  # full pages in every request
+    announce(f"quest shared prefix {name} seed {wl.seed} lens {lens} shared pages {shared}")
+    x = make_quest_inputs(wl, DEV, poison_tail=True, seq_lens=lens, pool_extra=5)
+    assert min(lens) > 16 * shared
+    x["page_table"][1:, :shared] = x["page_table"][0, :shared]
+    summ = build_summaries(x, wl)
+    out, sel = run_sparse_decode(x, wl, summ)
+    h = host_inputs(x)
+    ref_summ = oracle.quest_summaries(h["k"], h["pt"], h["lens"])
+    got = oracle.bf16_to_f64(bf16_bits(summ))
+    for b, n in enumerate(h["lens"]):
+        P = -(-int(n) // 16)
+        np.testing.assert_array_equal(got[h["pt"][b, :P]], ref_summ[b, :P])
+    A = oracle.quest_scores(h["q"], ref_summ, h["lens"], wl.group, wl.scale)
+    sel_np = to_np(sel)
+    for b, n in enumerate(h["lens"]):
+        Pb = -(-int(n) // 16)
+        for g in range(wl.num_kv_heads):
+            check_selection(sel_np[b, g], A[b, g, :Pb], wl.topk, f"shared {name} b{b} g{g}")
+    ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], sel_lists(sel_np, h["lens"]), wl.group,
+                                  wl.scale, wl.head_dim_v, wl.v_is_k_prefix)
+    vmax = float(torch.nan_to_num(x["v_pages"] if x["v_pages"] is not None else x["k_pages"], 0.0).abs().max())
+    check_attention(to_np(out), ref, vmax, f"shared {name}")

@@ -128,23 +128,10 @@ def main():
     torch.cuda.synchronize()
 
     lens = x["seq_lens"].cpu().numpy().astype(np.int64)
-    pages = (lens + 15) // 16
-    kept = np.minimum(pages, kcap)
-    # algorithmic bytes of one step
-    row_k = Dk * 2
-    row_v = 0 if wl.v_is_k_prefix else Dv * 2
-    # tokens of the kept pages; the partial last page counts its valid tokens
-    # when it is kept for sure (all pages kept, or recent pages forced)
-    tok_kept = sum(int(16 * (k - 1) + n - 16 * (p - 1)) if (k == p or recent > 0) else int(16 * k)
-                   for n, k, p in zip(lens, kept, pages))
     scored = topk > 0
-    bytes_q = B * Hq * Dk * 2
-    bytes_summ = int(pages.sum()) * Hkv * 2 * Dk * 2 if scored else 0
-    bytes_pt = int(pages.sum()) * 4 if scored else int(kept.sum()) * 4
-    bytes_kv = tok_kept * Hkv * (row_k + row_v)
-    bytes_out = B * Hq * Dv * 4
-    b_alg = bytes_q + bytes_summ + bytes_pt + bytes_kv + bytes_out
-    bytes_k1 = bytes_q + bytes_summ + bytes_pt + int(pages.sum()) * Hkv * 4  # + scores written
+    alg = quest_algorithmic_bytes(lens, Hq, Hkv, Dk, Dv, wl.v_is_k_prefix, topk, kcap, recent)
+    b_alg, bytes_k1 = alg["step"], alg["scorer_launch"]
+    bytes_q, bytes_kv, bytes_out = alg["q"], alg["kv"], alg["out"]
 
     def step(i):
         q = qs[i % nq]
@@ -233,6 +220,30 @@ def main():
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, x, qs, args.cpu_seconds, topk, sink, recent)
     print(json.dumps(result))
+
+
+def quest_algorithmic_bytes(lens, Hq, Hkv, Dk, Dv, v_is_k_prefix, topk, kcap, recent=0) -> dict:
+    """The bytes one Quest decode step must move (q, the summaries of every
+    valid page, the page table, the valid tokens of the kept pages' K and V
+    -- the latent row once when V is a prefix of K -- and the output), and
+    those of one scorer launch (q, summaries, page table, scores written).
+    A kept partial last page counts its valid tokens when it is kept for
+    sure (all pages kept, or recent pages forced), else 16 tokens."""
+    lens = [int(n) for n in lens]
+    B = len(lens)
+    pages = [(n + 15) // 16 for n in lens]
+    kept = [min(p, kcap) for p in pages]
+    row = Dk * 2 + (0 if v_is_k_prefix else Dv * 2)
+    tok_kept = sum(16 * (k - 1) + n - 16 * (p - 1) if (k == p or recent > 0) else 16 * k
+                   for n, k, p in zip(lens, kept, pages))
+    scored = topk > 0
+    q = B * Hq * Dk * 2
+    summ = sum(pages) * Hkv * 2 * Dk * 2 if scored else 0
+    pt = sum(pages) * 4 if scored else sum(kept) * 4
+    kv = tok_kept * Hkv * row
+    out = B * Hq * Dv * 4
+    return {"q": q, "summaries": summ, "page_table": pt, "kv": kv, "out": out, "step": q + summ + pt + kv + out,
+            "scorer_launch": q + summ + pt + sum(pages) * Hkv * 4}
 
 
 def counted_bytes(workload: str, t_step: float, forced: bool) -> dict:

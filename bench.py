@@ -630,8 +630,9 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 def votes_roofline(b_votes, flops_votes, t_votes, traffic):
     """Roofline of the window x context scoring (row statistics + votes): the
     bound is the one its arithmetic intensity puts it under -- HBM below the
-    bf16 ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B; SnapKV's 32-row window,
-    128 flop/B), the matrix cores above it (H2O's 128-row window, 512 flop/B)."""
+    bf16 ridge (2.5 PFLOP/s / 8 TB/s = 312 flop/B; SnapKV's 32-row window
+    over a 32K prompt, 251 flop/B over both passes), the matrix cores above it
+    (H2O's 128-row window, 993 flop/B)."""
     intensity = flops_votes / b_votes
     gbps = b_votes / t_votes / 1e9
     tflops = flops_votes / t_votes / 1e12

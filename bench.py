@@ -444,10 +444,7 @@ def bench_snapkv(args, wl):
     tokens_s = B * S / t_whole
     # algorithmic bytes: the window queries, K once, the kept K/V rows read and
     # written, the kept ids; then per decode step the attended rows, q and out
-    rows_dec = sum(kl + s + 1 for s in range(S))
-    b_evict = B * Hq * W * D * 2 + B * H * n * D * 2 + 2 * 2 * B * H * kl * D * 2 + B * H * kl * 4
-    b_dec = B * H * rows_dec * 2 * D * 2 + S * (B * Hq * D * 2 + B * Hq * D * 4)
-    b_votes = B * Hq * W * D * 2 + B * H * n * D * 2 + B * H * n * 4
+    b_evict, b_dec, b_votes = snapkv_algorithmic_bytes(B, Hq, H, D, n, W, kl, S)
     # window x context scores: pass 1 over every key, pass 2 over the columns
     # whose votes the selection reads (the candidates plus the pooling halo)
     ib, ie = wl.interval if wl.interval[1] else (0, n)
@@ -622,6 +619,19 @@ def bench_pyramid(args, wl):
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_snapkv(wl, x, args.cpu_seconds, budgets)
     print(json.dumps(result))
+
+
+def snapkv_algorithmic_bytes(B, Hq, H, D, n, W, kl, S):
+    """Bytes an eviction must move (the window queries, K once, the kept K
+    and V rows read and written, the kept ids), those of S decode steps over
+    the retained cache (step s attends kl + s + 1 rows of K and V; q in, out
+    as fp32), and those of the votes pass (window queries, K once, votes
+    written)."""
+    b_evict = B * Hq * W * D * 2 + B * H * n * D * 2 + 2 * 2 * B * H * kl * D * 2 + B * H * kl * 4
+    rows_dec = sum(kl + s + 1 for s in range(S))
+    b_dec = B * H * rows_dec * 2 * D * 2 + S * (B * Hq * D * 2 + B * Hq * D * 4)
+    b_votes = B * Hq * W * D * 2 + B * H * n * D * 2 + B * H * n * 4
+    return b_evict, b_dec, b_votes
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0

@@ -44,3 +44,19 @@ def test_nothing_scored_reads_only_the_kept_page_table_entries():
     a = bench.quest_algorithmic_bytes([160] * 2, 8, 2, 128, 128, False, 0, 3)
     assert a["summaries"] == 0
     assert a["page_table"] == 2 * 3 * 4
+
+
+def test_snapkv_workload_bytes():
+    # B16, Hq32, Hkv8, D128, 32768-token prompts, window 32, 2,080 rows kept,
+    # 64 decode steps
+    ev, dec, votes = bench.snapkv_algorithmic_bytes(16, 32, 8, 128, 32768, 32, 2080, 64)
+    q_win = 16 * 32 * 32 * 128 * 2                 # 4.2 MB
+    k_once = 16 * 8 * 32768 * 256                  # 1,073.7 MB
+    kept_rw = 2 * 2 * 16 * 8 * 2080 * 256          # K and V rows read and written, 272.6 MB
+    assert ev == q_win + k_once + kept_rw + 16 * 8 * 2080 * 4
+    assert round(ev / 1e6) == 1352
+    # step s attends 2081 + s rows: 136.4 MB at the first step
+    first = 16 * 8 * 2081 * 512 + 16 * 32 * 128 * 6
+    assert dec == sum(16 * 8 * (2081 + s) * 512 for s in range(64)) + 64 * 16 * 32 * 128 * 6
+    assert dec > 64 * first
+    assert votes == q_win + k_once + 16 * 8 * 32768 * 4

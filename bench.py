@@ -36,11 +36,13 @@ def parse():
     ap.add_argument("--workload", default="gqa32x4_d128_128k_b32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="CPU time the oracle baseline spends on sampled (request, KV head) units")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="time each oracle-baseline worker spends on its sampled (request, KV head) units")
     ap.add_argument("--topk", type=int, default=None, help="pages selected by score (default: the workload's)")
     ap.add_argument("--sink-pages", type=int, default=0, help="leading pages every request always keeps")
     ap.add_argument("--recent-pages", type=int, default=0, help="trailing pages every request always keeps")
+    ap.add_argument("--valu-attention", action="store_true",
+                    help="run the attention on the vector-ALU kernel instead of the matrix cores")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (HBM byte-counter calibration)")
     return ap.parse_args()
@@ -109,9 +111,10 @@ def main():
     se.se_build_summaries(L, B, MP, x["k_pages"], x["page_table"], x["seq_lens"], summ)
     topk = wl.topk if args.topk is None else args.topk
     sink, recent = args.sink_pages, args.recent_pages
-    forced = sink > 0 or recent > 0 or topk != wl.topk
+    forced = sink > 0 or recent > 0 or topk != wl.topk or args.valu_attention
     # topk = 0 keeps the forced pages only: nothing is scored or refreshed
-    P = se.decode_params(B, Hq, MP, topk, wl.scale, 0, 1 if topk > 0 else 0, 0, sink, recent)
+    P = se.decode_params(B, Hq, MP, topk, wl.scale, 0, 1 if topk > 0 else 0, 0, sink, recent,
+                         valu_attention=int(args.valu_attention))
     kcap = se.kept_capacity(P)
     ws = torch.empty(se.se_sparse_decode_workspace_size(L, P), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, Dv), dtype=torch.float32, device=dev)
@@ -169,7 +172,9 @@ def main():
     bytes_k34 = bytes_q + bytes_kv + bytes_out
     k34_gbps = bytes_k34 / t_k34 / 1e9
 
-    variant = f", sink {sink} + recent {recent} + top {topk} pages" if forced else ""
+    variant = f", sink {sink} + recent {recent} + top {topk} pages" if (sink or recent or topk != wl.topk) else ""
+    if args.valu_attention:
+        variant += ", vector-ALU attention"
     if scored:
         roofline = {"kernel": "quest_score (page scoring + last-page refresh)", "bound": "hbm",
                     "achieved": round(k1_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -198,7 +203,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "context": wl.context, "num_q_heads": Hq, "num_kv_heads": Hkv,
                    "head_dim_qk": Dk, "head_dim_v": Dv, "page_tokens": 16, "topk_pages": topk,
-                   "sink_pages": sink, "recent_pages": recent, "saliency": wl.saliency},
+                   "sink_pages": sink, "recent_pages": recent, "saliency": wl.saliency,
+                   "attention_kernel": "vector ALU" if args.valu_attention else "matrix cores where built"},
         "effective_hbm_gbps": round(gbps, 1),
         "pct_peak_hbm": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_step": b_alg,
@@ -226,7 +232,7 @@ def quest_algorithmic_bytes(lens, Hq, Hkv, Dk, Dv, v_is_k_prefix, topk, kcap, re
     """The bytes one Quest decode step must move (q, the summaries of every
     valid page, the page table, the valid tokens of the kept pages' K and V
     -- the latent row once when V is a prefix of K -- and the output), and
-    those of one scorer launch (q, summaries, page table, scores written).
+    those of one scorer launch (q, summaries, page table).
     A kept partial last page counts its valid tokens when it is kept for
     sure (all pages kept, or recent pages forced), else 16 tokens."""
     lens = [int(n) for n in lens]
@@ -242,8 +248,10 @@ def quest_algorithmic_bytes(lens, Hq, Hkv, Dk, Dv, v_is_k_prefix, topk, kcap, re
     pt = sum(pages) * 4 if scored else sum(kept) * 4
     kv = tok_kept * Hkv * row
     out = B * Hq * Dv * 4
+    # one scorer launch reads q, the summaries and the page table; the page
+    # scores it writes are an intermediate of the step and are not counted
     return {"q": q, "summaries": summ, "page_table": pt, "kv": kv, "out": out, "step": q + summ + pt + kv + out,
-            "scorer_launch": q + summ + pt + sum(pages) * Hkv * 4}
+            "scorer_launch": q + summ + pt}
 
 
 def counted_bytes(workload: str, t_step: float, forced: bool) -> dict:
@@ -290,9 +298,9 @@ def stream_read_reference(torch, gbps):
     effective rate as a fraction of it."""
     import ctypes
     import numpy as np
-    from sparse_kv_long_amd.probe.build import PROBE_LIB
+    from stream_read.build import PROBE_LIB
     if not os.path.exists(PROBE_LIB):
-        raise RuntimeError(f"{PROBE_LIB} is missing: build it first (python -m sparse_kv_long_amd.probe.build)")
+        raise RuntimeError(f"{PROBE_LIB} is missing: build it first (python -m stream_read.build)")
     h = ctypes.CDLL(PROBE_LIB)
     h.se_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     h.se_hbm_read.restype = ctypes.c_int
@@ -625,12 +633,12 @@ def snapkv_algorithmic_bytes(B, Hq, H, D, n, W, kl, S):
     """Bytes an eviction must move (the window queries, K once, the kept K
     and V rows read and written, the kept ids), those of S decode steps over
     the retained cache (step s attends kl + s + 1 rows of K and V; q in, out
-    as fp32), and those of the votes pass (window queries, K once, votes
-    written)."""
+    as fp32), and those of the votes pass (window queries, K once; the votes
+    it writes are an intermediate of the eviction and are not counted)."""
     b_evict = B * Hq * W * D * 2 + B * H * n * D * 2 + 2 * 2 * B * H * kl * D * 2 + B * H * kl * 4
     rows_dec = sum(kl + s + 1 for s in range(S))
     b_dec = B * H * rows_dec * 2 * D * 2 + S * (B * Hq * D * 2 + B * Hq * D * 4)
-    b_votes = B * Hq * W * D * 2 + B * H * n * D * 2 + B * H * n * 4
+    b_votes = B * Hq * W * D * 2 + B * H * n * D * 2
     return b_evict, b_dec, b_votes
 
 
@@ -659,45 +667,83 @@ def votes_roofline(b_votes, flops_votes, t_votes, traffic):
     return r
 
 
-def cpu_baseline_snapkv(wl, x, seconds, budgets=None):
-    """The oracle's eviction (votes, pool, keep, row copies) and its decode
-    steps over the kept rows, per (request, KV head) unit on one thread, until
-    about `seconds` of CPU time are spent; scaled to the batch."""
+def _baseline_workers() -> int:
+    """Worker processes for the oracle baseline: the host CPUs this process
+    may run on, at most 16 (one GPU's share of a shared host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def _run_baseline_pool(fn, shares, seconds):
+    """fn(share, seconds) in one spawned worker process per share (the workers
+    import numpy and the oracle only, never the GPU); returns their results."""
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+    with ProcessPoolExecutor(max_workers=len(shares), mp_context=multiprocessing.get_context("spawn")) as ex:
+        futs = [ex.submit(fn, sh, seconds) for sh in shares]
+        return [f.result() for f in futs]
+
+
+def _snapkv_baseline_worker(units, seconds):
+    """One worker of the eviction baseline: the oracle's eviction and decode
+    steps on its staged units, cycling through them, on one thread, until
+    `seconds` of measured time; returns (units done, seconds measured)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
+    spent, done = 0.0, 0
+    with threadpool_limits(1):
+        while spent < seconds:
+            u = units[done % len(units)]
+            G, W, S, n, R, scale, pool, sink, recent, interval = u["cfg"]
+            t0 = time.perf_counter()
+            Sv, _, _ = oracle.snapkv_unit_votes(oracle.bf16_to_f64(u["qw"]), oracle.bf16_to_f64(u["k"]), n, scale)
+            keep = oracle.eviction_unit_keep(oracle.maxpool1d(Sv, pool), n, W, R, sink, recent, interval)
+            kc = np.concatenate([u["k"][keep], u["ks"]])[None]
+            vc = np.concatenate([u["v"][keep], u["vs"]])[None]
+            for s in range(S):
+                oracle.decode_over_rows(u["qs"][s], kc, vc, len(keep) + s + 1, G, scale)
+            spent += time.perf_counter() - t0
+            done += 1
+    return done, spent
+
+
+def cpu_baseline_snapkv(wl, x, seconds, budgets=None):
+    """The oracle's eviction (votes, pool, keep, row copies) and its decode
+    steps over the kept rows, per (layer, request, KV head) unit, in one
+    single-threaded worker process per host core (at most 16), each timing
+    about `seconds` of its own units; the units/s of the workers add up and
+    are scaled to the batch."""
+    import numpy as np
+
     from synth import bf16_bits
 
     G, W, S, n = wl.group, wl.window, wl.decode_steps, wl.prompt
     budgets = budgets or [wl.budget]
-    # (layer, request, KV head) units; one layer unless the workload has several
     units = [(R, b, g) for R in budgets for b in range(wl.batch) for g in range(wl.num_kv_heads)]
     order = np.random.default_rng(0).permutation(len(units))
-    spent, done = 0.0, 0
-    while spent < seconds and done < len(units):
-        R, b, g = units[int(order[done])]
-        qw = bf16_bits(x["q_win"][b, g * G:(g + 1) * G])
-        kb, vb = bf16_bits(x["k"][b, g]), bf16_bits(x["v"][b, g])
-        qs = bf16_bits(x["q_steps"][:, b, g * G:(g + 1) * G])
-        ks, vs = bf16_bits(x["k_steps"][:, b, g]), bf16_bits(x["v_steps"][:, b, g])
-        with threadpool_limits(1):
-            t0 = time.perf_counter()
-            Sv, _, _ = oracle.snapkv_unit_votes(oracle.bf16_to_f64(qw), oracle.bf16_to_f64(kb), n, wl.scale)
-            keep = oracle.eviction_unit_keep(oracle.maxpool1d(Sv, wl.pool_kernel), n, W, R, wl.sink, wl.recent,
-                                             wl.interval if wl.interval[1] else None)
-            kc = np.concatenate([kb[keep], ks])[None]
-            vc = np.concatenate([vb[keep], vs])[None]
-            for s in range(S):
-                oracle.decode_over_rows(qs[s], kc, vc, len(keep) + s + 1, G, wl.scale)
-            spent += time.perf_counter() - t0
-        done += 1
-    step_s = spent / done * len(units)
+    N = min(_baseline_workers(), len(units))
+    per = 2 if len(units) >= 2 * N else 1
+    interval = wl.interval if wl.interval[1] else None
+    shares = [[] for _ in range(N)]
+    for i in range(N * per):  # staged before timing: the bf16 bits each unit reads
+        R, b, g = units[int(order[i])]
+        shares[i % N].append({
+            "cfg": (G, W, S, n, R, wl.scale, wl.pool_kernel, wl.sink, wl.recent, interval),
+            "qw": bf16_bits(x["q_win"][b, g * G:(g + 1) * G]), "k": bf16_bits(x["k"][b, g]),
+            "v": bf16_bits(x["v"][b, g]), "qs": bf16_bits(x["q_steps"][:, b, g * G:(g + 1) * G]),
+            "ks": bf16_bits(x["k_steps"][:, b, g]), "vs": bf16_bits(x["v_steps"][:, b, g])})
+    res = _run_baseline_pool(_snapkv_baseline_worker, shares, seconds)
+    rate = sum(d / t for d, t in res)  # units per second over the workers
+    step_s = len(units) / rate
     what = "(layer, request, KV head)" if len(budgets) > 1 else "(request, KV head)"
-    return {"value": round(wl.batch * S / step_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {len(units)} {what} units: fp64 numpy on one thread, votes over the "
-                      f"32K prompt, pool, keep, row copies and {S} decode steps each; {spent:.1f} s measured, "
-                      f"scaled by units to the batch"}
+    return {"value": round(wl.batch * S / step_s, 3), "unit": "tokens/s", "cores": N, "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{sum(d for d, _ in res)} {what} unit evictions ({len(units)} make one step) by {N} "
+                      f"single-threaded fp64 numpy worker processes, {N * per} distinct units: votes over the "
+                      f"{n}-token prompt, pool, keep, row copies and {S} decode steps each; "
+                      f"{sum(t for _, t in res):.1f} s measured in all, the workers' units/s summed and scaled to "
+                      f"the batch"}
 
 
 def copy_calibration(torch):
@@ -714,17 +760,55 @@ def copy_calibration(torch):
     print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4}))
 
 
-def cpu_baseline(wl, x, qs, seconds, topk, sink=0, recent=0):
-    """Time the oracle's decode step (page bounds, KV-head scores, selection,
-    attention -- given the page summaries, which the oracle builds beforehand,
-    untimed -- including the decoding of the bf16 inputs it reads) on (request, KV head) units in a seeded order,
-    single-threaded, until about `seconds` of CPU time are spent (passing on
-    to the next query once every unit of a step is done, cycling through the
-    queries), and scale to the whole step."""
+def _quest_baseline_worker(units, seconds):
+    """One worker of the decode baseline: builds its units' page summaries with
+    the oracle (prefill side, untimed), then times the oracle's decode step
+    (bf16 decoding of what it reads, page bounds, KV-head max, selection,
+    attention) on them, cycling through units and queries, on one thread,
+    until `seconds` of measured time; returns (units done, seconds measured)."""
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle
+    with threadpool_limits(1):
+        for u in units:
+            P = oracle.pages_of(u["n"])
+            u["summ"] = oracle.unit_summaries(oracle.gather_unit_pages(u["k"][:, None], np.arange(P), 0, u["n"]),
+                                              u["n"])
+        spent, done = 0.0, 0
+        while spent < seconds:
+            u = units[done % len(units)]
+            G, scale, topk, sink, recent, dv = u["cfg"]
+            qh = u["q"][(done // len(units)) % len(u["q"])]
+            n = u["n"]
+            mins, maxs = u["summ"]
+            t0 = time.perf_counter()
+            qf = oracle.bf16_to_f64(qh)
+            if topk > 0:
+                A = oracle.unit_kv_head_score(oracle.unit_page_bounds(qf, mins, maxs, scale))
+            else:  # forced pages only: nothing is scored
+                A = np.zeros(len(mins))
+            sel = (oracle.unit_select_forced(A, topk, sink, recent) if sink or recent else oracle.unit_select(A, topk))
+            kp = oracle.bf16_to_f64(u["k"])
+            vp = kp[..., :dv] if u["v"] is None else oracle.bf16_to_f64(u["v"])
+            keys = oracle.unit_selected_tokens(kp, sel, n)
+            vals = oracle.unit_selected_tokens(vp, sel, n)
+            oracle.unit_attention(qf, keys, vals, scale)
+            spent += time.perf_counter() - t0
+            done += 1
+    return done, spent
+
+
+def cpu_baseline(wl, x, qs, seconds, topk, sink=0, recent=0):
+    """Time the oracle's decode step (page bounds, KV-head scores, selection,
+    attention -- given the page summaries, which the oracle builds
+    beforehand, untimed -- including the decoding of the bf16 inputs it reads)
+    on (request, KV head) units in one single-threaded worker process per host
+    core (at most 16), each on two units staged beforehand, cycling through
+    the benchmark's queries, for about `seconds`; the workers' units/s add up
+    and are scaled to the whole step."""
+    import numpy as np
+
     from synth import bf16_bits
 
     G = wl.group
@@ -732,42 +816,31 @@ def cpu_baseline(wl, x, qs, seconds, topk, sink=0, recent=0):
     order = np.random.default_rng(0).permutation(len(units))
     pt = x["page_table"].cpu().numpy()
     lens = x["seq_lens"].cpu().numpy()
-    spent = 0.0
-    done = 0
-    summaries = {}
-    while spent < seconds and done < 100000:
-        b, g = units[int(order[done % len(units)])]
-        qh = bf16_bits(qs[(done // len(units)) % len(qs)][b])
+    N = min(_baseline_workers(), len(units))
+    per = 2 if len(units) >= 2 * N else 1
+    nq = min(len(qs), 8)
+    qbits = bf16_bits(qs[:nq])
+    shares = [[] for _ in range(N)]
+    for i in range(N * per):  # staged before timing: the bf16 bits each unit reads
+        b, g = units[int(order[i])]
         n = int(lens[b])
         P = -(-n // 16)
-        rows = torch_index(x["k_pages"], pt[b, :P], g)
-        vrows = None if x["v_pages"] is None else torch_index(x["v_pages"], pt[b, :P], g)
-        if (b, g) not in summaries:  # prefill side (O1), untimed, by the oracle itself
-            summaries[(b, g)] = oracle.unit_summaries(oracle.gather_unit_pages(rows[:, None], np.arange(P), 0, n), n)
-        mins, maxs = summaries[(b, g)]
-        with threadpool_limits(1):
-            t0 = time.perf_counter()
-            qf = oracle.bf16_to_f64(qh[g * G:(g + 1) * G])
-            if topk > 0:
-                U = oracle.unit_page_bounds(qf, mins, maxs, wl.scale)
-                A = oracle.unit_kv_head_score(U)
-            else:  # forced pages only: nothing is scored
-                A = np.zeros(P)
-            s = (oracle.unit_select_forced(A, topk, sink, recent) if sink or recent else oracle.unit_select(A, topk))
-            kp = oracle.bf16_to_f64(rows)
-            vp = kp[..., :wl.head_dim_v] if vrows is None else oracle.bf16_to_f64(vrows)
-            keys = oracle.unit_selected_tokens(kp, s, n)
-            vals = oracle.unit_selected_tokens(vp, s, n)
-            oracle.unit_attention(qf, keys, vals, wl.scale)
-            spent += time.perf_counter() - t0
-        done += 1
-    per_unit = spent / done
-    step_s = per_unit * len(units)
-    return {"value": round(wl.batch / step_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} (request, KV head) units ({len(units)} make one decode step), fp64 numpy on one "
-                      f"thread: bf16 decoding of the unit's query and K/V pages, page bounds from the oracle's own page "
-                      f"summaries (built untimed), KV-head max, "
-                      f"top-k and attention; {spent:.1f} s measured, scaled by units to the step"}
+        shares[i % N].append({
+            "cfg": (G, wl.scale, topk, sink, recent, wl.head_dim_v), "n": n,
+            "q": qbits[:, b, g * G:(g + 1) * G],
+            "k": torch_index(x["k_pages"], pt[b, :P], g),
+            "v": None if x["v_pages"] is None else torch_index(x["v_pages"], pt[b, :P], g)})
+    res = _run_baseline_pool(_quest_baseline_worker, shares, seconds)
+    rate = sum(d / t for d, t in res)  # units per second over the workers
+    step_s = len(units) / rate
+    return {"value": round(wl.batch / step_s, 3), "unit": "tokens/s", "cores": N, "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{sum(d for d, _ in res)} (request, KV head) unit steps ({len(units)} make one decode step) "
+                      f"by {N} single-threaded fp64 numpy worker processes on {N * per} distinct units and {nq} "
+                      f"queries: bf16 decoding of the unit's query and K/V pages, page bounds from the oracle's own "
+                      f"page summaries (built untimed), KV-head max, top-k and attention; "
+                      f"{sum(t for _, t in res):.1f} s measured in all, the workers' units/s summed and scaled to "
+                      f"the step"}
 
 
 def torch_index(pages, phys, g):

@@ -103,6 +103,12 @@ typedef struct se_decode_params {
                                  request are always kept                      */
   int32_t recent_pages;       /* >= 0: the last recent_pages pages of every
                                  request are always kept                      */
+  int32_t valu_attention;     /* 0: the attention runs on the matrix cores
+                                 where a kernel for the shape is built (Dk =
+                                 Dv = 128 with G <= 16, and the 576/512 latent
+                                 layout); 1: the vector-ALU dot-product kernel
+                                 for every shape, which leaves the matrix
+                                 cores to other work (slower here)           */
 } se_decode_params;
 /* Forced pages (SparseEngine appendix Tables 8-11: a sink and a recent budget
  * beside each method's selected budget, which excludes them; the StreamingLLM

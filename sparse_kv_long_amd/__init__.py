@@ -43,7 +43,8 @@ class DecodeParams(ctypes.Structure):
                 ("max_pages_per_seq", ctypes.c_int32), ("topk", ctypes.c_int32),
                 ("sm_scale", ctypes.c_float), ("head_agg", ctypes.c_int32),
                 ("refresh_last_page", ctypes.c_int32), ("num_splits", ctypes.c_int32),
-                ("sink_pages", ctypes.c_int32), ("recent_pages", ctypes.c_int32)]
+                ("sink_pages", ctypes.c_int32), ("recent_pages", ctypes.c_int32),
+                ("valu_attention", ctypes.c_int32)]
 
 
 class SnapKVParams(ctypes.Structure):
@@ -145,9 +146,10 @@ def dense_layout(num_kv_heads: int, capacity: int, head_dim: int) -> KvLayout:
 
 
 def decode_params(batch, num_q_heads, max_pages_per_seq, topk, sm_scale=0.0, head_agg=0,
-                  refresh_last_page=0, num_splits=0, sink_pages=0, recent_pages=0) -> DecodeParams:
+                  refresh_last_page=0, num_splits=0, sink_pages=0, recent_pages=0,
+                  valu_attention=0) -> DecodeParams:
     return DecodeParams(batch, num_q_heads, max_pages_per_seq, topk, sm_scale, head_agg, refresh_last_page,
-                        num_splits, sink_pages, recent_pages)
+                        num_splits, sink_pages, recent_pages, valu_attention)
 
 
 def kept_capacity(params: DecodeParams) -> int:

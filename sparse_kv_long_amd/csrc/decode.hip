@@ -18,9 +18,6 @@
 //            groups are then folded together with cross-lane shuffles.
 // The split writes (max, sum, unnormalised acc); the merge kernel combines the
 // splits of each head: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
-#include <stdlib.h>
-#include <string.h>
-
 #include "common.h"
 #include "se_internal.h"
 
@@ -892,7 +889,7 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
 // into weights w_s = 2^(m_s - M) / sum_s' 2^(m_s' - M) l_s' (0 for an empty
 // split) in LDS; then every thread sums w_s acc_s for its channels with all
 // loads unconditional, so they are issued back to back.
-constexpr int kMaxSplits = 1024;
+constexpr int kMaxSplits = 4096;  // splits * pages per split covers 65536 pages at 16 per split
 
 // Few splits (the common case): every thread loads all (m, l) pairs of its
 // (request, head) and four acc columns of every split at once, so the merge
@@ -1018,28 +1015,27 @@ static hipError_t launch_merge(const DecodeArgs& a, int DV, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
-bool use_mfma_decode();
-
-static bool mfma_decode_shape(const Layout& L, int G) {
-  return L.dk == 128 && L.dv == 128 && !L.visk && G <= 16 && use_mfma_decode();
+static bool mfma_decode_shape(const Layout& L, int G, bool valu) {
+  return L.dk == 128 && L.dv == 128 && !L.visk && G <= 16 && !valu;
 }
 
-static bool mla_decode_shape(const Layout& L, int G) {
-  return L.dk == 576 && L.dv == 512 && L.visk && G <= 32 && use_mfma_decode();
+static bool mla_decode_shape(const Layout& L, int G, bool valu) {
+  return L.dk == 576 && L.dv == 512 && L.visk && G <= 32 && !valu;
 }
 
-static int max_pps(const Layout& L, int G) {
-  if (mfma_decode_shape(L, G)) return G <= 8 ? 256 : 128;
-  if (mla_decode_shape(L, G)) return kMlaPagesPerSplit;
+int decode_max_pps(const Layout& L, int G, bool valu) {
+  if (mfma_decode_shape(L, G, valu)) return G <= 8 ? 256 : 128;
+  if (mla_decode_shape(L, G, valu)) return kMlaPagesPerSplit;
   return (L.dk <= 128 && G <= 16) ? 32 : 16;
 }
 
-int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, int requested) {
+int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, int requested, bool valu) {
   // pages attended per (request, KV head) at most
   const int kmax = (dense || topk >= MP) ? MP : topk;
   if (kmax <= 0) return 1;
   const int units = B * L.hkv;
-  const int mp = max_pps(L, Hq / L.hkv);
+  const int G = Hq / L.hkv;
+  const int mp = decode_max_pps(L, G, valu);
   const int smin = (kmax + mp - 1) / mp;
   // about one block per CU for the matrix-core GQA decode (measured at 128K,
   // 256 kept pages: 2 splits = 256 blocks 54.3 us with the merge, 4 splits =
@@ -1047,15 +1043,14 @@ int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, 
   // CUs idle), one full round of resident blocks for the others (x 4 for the
   // VALU kernel); more splits only add per-block latency and merge traffic, a
   // partial second round idles the chip
-  const int G = Hq / L.hkv;
-  const int target = mla_decode_shape(L, G) ? kMlaTargetBlocks / ((G + kMlaHeadsPerBlock - 1) / kMlaHeadsPerBlock)
-                     : mfma_decode_shape(L, G) ? 256 : 1024;
+  const int target = mla_decode_shape(L, G, valu) ? kMlaTargetBlocks / ((G + kMlaHeadsPerBlock - 1) / kMlaHeadsPerBlock)
+                     : mfma_decode_shape(L, G, valu) ? 256 : 1024;
   int s = requested > 0 ? requested : (target + units - 1) / units;
   // the matrix-core GQA decode keeps at least 32 pages (8 per wave) per split
   // while that still gives every CU a block: fewer leave each block with more
   // fixed cost than streaming (measured at 32K, 128 kept pages: 23.0 us with 4
   // splits, 28.5 us with 8)
-  if (requested <= 0 && mfma_decode_shape(L, G)) {
+  if (requested <= 0 && mfma_decode_shape(L, G, valu)) {
     const int s32 = kmax / 32 > 0 ? kmax / 32 : 1;
     if ((int64_t)units * s32 >= 256 && s > s32) s = s32;
   }
@@ -1127,23 +1122,15 @@ static hipError_t launch_mla(const Layout& L, const DecodeArgs& a, int pps, hipS
 }
 
 // Decode path: the matrix-core kernels for Dk = Dv = 128 with G <= 16 and for
-// the MLA layout with G <= 32, unless SE_DECODE=valu; the VALU kernel for
-// every other shape.
-bool use_mfma_decode() {
-  static const bool v = [] {
-    const char* e = getenv("SE_DECODE");
-    return !(e && strcmp(e, "valu") == 0);
-  }();
-  return v;
-}
-
+// the MLA layout with G <= 32, unless the caller asks for the vector-ALU
+// kernel (valu); the vector-ALU kernel for every other shape.
 hipError_t launch_decode(const Layout& L, const DecodeArgs& a, hipStream_t st) {
   if (a.B == 0) return hipSuccess;
   const int G = a.Hq / L.hkv;
   const int kmax = a.selected ? (a.topk < a.MP ? a.topk : a.MP) : a.MP;
   const int pps = (kmax + a.splits - 1) / a.splits;
-  if (pps > max_pps(L, G)) return hipErrorInvalidValue;
-  if (mfma_decode_shape(L, G)) {
+  if (pps > decode_max_pps(L, G, a.valu)) return hipErrorInvalidValue;  // the host checks this before any launch
+  if (mfma_decode_shape(L, G, a.valu)) {
     switch (G) {
       case 1: return launch_mfma_g<1>(L, a, pps, st);
       case 2: return launch_mfma_g<2>(L, a, pps, st);
@@ -1153,7 +1140,7 @@ hipError_t launch_decode(const Layout& L, const DecodeArgs& a, hipStream_t st) {
       default: break;
     }
   }
-  if (mla_decode_shape(L, G)) return launch_mla(L, a, pps, st);
+  if (mla_decode_shape(L, G, a.valu)) return launch_mla(L, a, pps, st);
   if (L.dk == 64 && L.dv == 64 && !L.visk) return launch_d<64, 64, false>(L, a, G, pps, st);
   if (L.dk == 128 && L.dv == 128 && !L.visk) return launch_d<128, 128, false>(L, a, G, pps, st);
   if (L.dk == 576 && L.dv == 512 && L.visk) return launch_d<576, 512, true>(L, a, G, pps, st);

@@ -14,7 +14,7 @@ namespace {
 
 using se::Layout;
 
-constexpr int kVersion = 300;  // 0.3.0: eviction family (sink/recent, interval, re-eviction), layer budgets
+constexpr int kVersion = 400;  // 0.4.0: explicit vector-ALU attention switch in se_decode_params
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -70,6 +70,7 @@ int check_params(const se_kv_layout* L, const se_decode_params* p) {
   if (p->head_agg != 0 && p->head_agg != 1) return SE_EINVAL;
   if (p->refresh_last_page != 0 && p->refresh_last_page != 1) return SE_EINVAL;
   if (p->num_splits < 0) return SE_EINVAL;
+  if (p->valu_attention != 0 && p->valu_attention != 1) return SE_EINVAL;
   return SE_OK;
 }
 
@@ -80,14 +81,16 @@ float eff_scale(const se_kv_layout* L, const se_decode_params* p) {
 struct DecodeWs {
   size_t scores, sel, phys, acc, ml, total;
   int splits;
+  bool fits;  // every split holds no more pages than its kernel can stage
 };
 
 DecodeWs decode_ws(const se_kv_layout* L, const se_decode_params* p, bool dense) {
   const Layout l = to_layout(L);
   DecodeWs w;
   const int B = p->batch, Hkv = L->num_kv_heads, MP = p->max_pages_per_seq;
-  w.splits = se::decode_splits(l, B, p->num_q_heads, MP, kept_cap(p), dense, p->num_splits);
-  const int s_other = se::decode_splits(l, B, p->num_q_heads, MP, kept_cap(p), !dense, p->num_splits);
+  const bool valu = p->valu_attention != 0;
+  w.splits = se::decode_splits(l, B, p->num_q_heads, MP, kept_cap(p), dense, p->num_splits, valu);
+  const int s_other = se::decode_splits(l, B, p->num_q_heads, MP, kept_cap(p), !dense, p->num_splits, valu);
   const int smax = w.splits > s_other ? w.splits : s_other;
   w.scores = 0;
   w.sel = w.scores + align256((size_t)B * Hkv * MP * sizeof(float));
@@ -95,6 +98,12 @@ DecodeWs decode_ws(const se_kv_layout* L, const se_decode_params* p, bool dense)
   w.acc = w.phys + align256((size_t)B * Hkv * kept_cap(p) * sizeof(int32_t));
   w.ml = w.acc + align256((size_t)B * p->num_q_heads * smax * L->head_dim_v * sizeof(float));
   w.total = w.ml + align256((size_t)B * p->num_q_heads * smax * 2 * sizeof(float));
+  // pages per split of the chosen split count, for the dense and the sparse
+  // page count, against what one block of the chosen kernel stages
+  const int G = p->num_q_heads / Hkv, mp = se::decode_max_pps(l, G, valu);
+  const int kd = MP, ks = kept_cap(p) < MP ? kept_cap(p) : MP;
+  const int k_this = dense ? kd : ks, k_other = dense ? ks : kd;
+  w.fits = (k_this + w.splits - 1) / w.splits <= mp && (k_other + s_other - 1) / s_other <= mp;
   return w;
 }
 
@@ -157,47 +166,7 @@ se::SnapArgs snap_args(const se_snapkv_params* p, const void* q_win, const void*
   return a;
 }
 
-}  // namespace
-
-extern "C" {
-
-int se_version(void) { return kVersion; }
-
-const char* se_status_string(int status) {
-  switch (status) {
-    case SE_OK: return "ok";
-    case SE_EINVAL: return "invalid argument";
-    case SE_EUNSUPPORTED: return "unsupported configuration";
-    case SE_EWORKSPACE: return "workspace missing or too small";
-    case SE_EHIP: return "HIP launch failed";
-    default: return "unknown status";
-  }
-}
-
-int se_build_summaries(const se_kv_layout* layout, int32_t batch, int32_t max_pages_per_seq, const void* k_pages,
-                       const int32_t* page_table, const int32_t* seq_lens, void* summaries, void* stream) {
-  int rc = check_layout(layout);
-  if (rc) return rc;
-  if (batch < 0 || max_pages_per_seq < 1) return SE_EINVAL;
-  if (batch == 0) return SE_OK;
-  if (!k_pages || !page_table || !seq_lens || !summaries) return SE_EINVAL;
-  if (!aligned16(k_pages) || !aligned16(summaries)) return SE_EINVAL;
-  return hip_status(se::launch_build_summaries(to_layout(layout), batch, max_pages_per_seq,
-                                               static_cast<const uint16_t*>(k_pages), page_table, seq_lens,
-                                               static_cast<uint16_t*>(summaries), (hipStream_t)stream));
-}
-
-int se_sparse_decode_workspace_size(const se_kv_layout* layout, const se_decode_params* params, size_t* bytes) {
-  int rc = check_layout(layout);
-  if (rc) return rc;
-  rc = check_params(layout, params);
-  if (rc) return rc;
-  if (!bytes) return SE_EINVAL;
-  *bytes = decode_ws(layout, params, kept_cap(params) >= params->max_pages_per_seq).total;
-  return SE_OK;
-}
-
-static int check_decode_ptrs(const se_kv_layout* layout, const void* q, const void* k_pages, const void* v_pages,
+int check_decode_ptrs(const se_kv_layout* layout, const void* q, const void* k_pages, const void* v_pages,
                              const int32_t* page_table, const int32_t* seq_lens, const float* out) {
   if (!q || !k_pages || !page_table || !seq_lens || !out) return SE_EINVAL;
   if (!layout->v_is_k_prefix && !v_pages) return SE_EINVAL;
@@ -206,9 +175,14 @@ static int check_decode_ptrs(const se_kv_layout* layout, const void* q, const vo
   return SE_OK;
 }
 
-int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params, const void* q, const void* k_pages,
-                     const void* v_pages, const int32_t* page_table, void* summaries, const int32_t* seq_lens,
-                     float* out, int32_t* selected, void* workspace, size_t workspace_bytes, void* stream) {
+}  // namespace
+
+namespace se {
+
+int sparse_decode_check(const se_kv_layout* layout, const se_decode_params* params, const void* q,
+                        const void* k_pages, const void* v_pages, const int32_t* page_table, const void* summaries,
+                        const int32_t* seq_lens, const float* out, size_t* need) {
+  *need = 0;
   int rc = check_layout(layout);
   if (rc) return rc;
   rc = check_params(layout, params);
@@ -216,16 +190,25 @@ int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params,
   if (params->batch == 0) return SE_OK;
   rc = check_decode_ptrs(layout, q, k_pages, v_pages, page_table, seq_lens, out);
   if (rc) return rc;
-  const int kcap = kept_cap(params);
-  const bool all_dense = kcap >= params->max_pages_per_seq;
+  const bool all_dense = kept_cap(params) >= params->max_pages_per_seq;
   // topk = 0 (sink and recent pages only) scores nothing
   const bool need_scores = (!all_dense && params->topk > 0) || params->refresh_last_page;
   if (need_scores && (!summaries || !aligned16(summaries))) return SE_EINVAL;
   const DecodeWs w = decode_ws(layout, params, all_dense);
-  if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return SE_EWORKSPACE;
+  if (!w.fits) return SE_EUNSUPPORTED;
+  *need = w.total;
+  return SE_OK;
+}
 
+int sparse_decode_enqueue(const se_kv_layout* layout, const se_decode_params* params, const void* q,
+                          const void* k_pages, const void* v_pages, const int32_t* page_table, void* summaries,
+                          const int32_t* seq_lens, float* out, int32_t* selected, void* workspace, hipStream_t st) {
+  int rc = SE_OK;
+  const int kcap = kept_cap(params);
+  const bool all_dense = kcap >= params->max_pages_per_seq;
+  const bool need_scores = (!all_dense && params->topk > 0) || params->refresh_last_page;
+  const DecodeWs w = decode_ws(layout, params, all_dense);
   const Layout L = to_layout(layout);
-  hipStream_t st = (hipStream_t)stream;
   char* ws = static_cast<char*>(workspace);
   float* scores = reinterpret_cast<float*>(ws + w.scores);
   int32_t* sel = selected ? selected : reinterpret_cast<int32_t*>(ws + w.sel);
@@ -273,7 +256,64 @@ int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params,
   d.topk = kcap;  // row length of the selection
   d.splits = w.splits;
   d.scale = scale;
+  d.valu = params->valu_attention != 0;
   return hip_status(se::launch_decode(L, d, st));
+}
+
+}  // namespace se
+
+extern "C" {
+
+int se_version(void) { return kVersion; }
+
+const char* se_status_string(int status) {
+  switch (status) {
+    case SE_OK: return "ok";
+    case SE_EINVAL: return "invalid argument";
+    case SE_EUNSUPPORTED: return "unsupported configuration";
+    case SE_EWORKSPACE: return "workspace missing or too small";
+    case SE_EHIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int se_build_summaries(const se_kv_layout* layout, int32_t batch, int32_t max_pages_per_seq, const void* k_pages,
+                       const int32_t* page_table, const int32_t* seq_lens, void* summaries, void* stream) {
+  int rc = check_layout(layout);
+  if (rc) return rc;
+  if (batch < 0 || max_pages_per_seq < 1) return SE_EINVAL;
+  if (batch == 0) return SE_OK;
+  if (!k_pages || !page_table || !seq_lens || !summaries) return SE_EINVAL;
+  if (!aligned16(k_pages) || !aligned16(summaries)) return SE_EINVAL;
+  return hip_status(se::launch_build_summaries(to_layout(layout), batch, max_pages_per_seq,
+                                               static_cast<const uint16_t*>(k_pages), page_table, seq_lens,
+                                               static_cast<uint16_t*>(summaries), (hipStream_t)stream));
+}
+
+int se_sparse_decode_workspace_size(const se_kv_layout* layout, const se_decode_params* params, size_t* bytes) {
+  int rc = check_layout(layout);
+  if (rc) return rc;
+  rc = check_params(layout, params);
+  if (rc) return rc;
+  if (!bytes) return SE_EINVAL;
+  const DecodeWs w = decode_ws(layout, params, kept_cap(params) >= params->max_pages_per_seq);
+  if (!w.fits) return SE_EUNSUPPORTED;
+  *bytes = w.total;
+  return SE_OK;
+}
+
+
+int se_sparse_decode(const se_kv_layout* layout, const se_decode_params* params, const void* q, const void* k_pages,
+                     const void* v_pages, const int32_t* page_table, void* summaries, const int32_t* seq_lens,
+                     float* out, int32_t* selected, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  const int rc = se::sparse_decode_check(layout, params, q, k_pages, v_pages, page_table, summaries, seq_lens, out,
+                                         &need);
+  if (rc) return rc;
+  if (params->batch == 0) return SE_OK;
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return SE_EWORKSPACE;
+  return se::sparse_decode_enqueue(layout, params, q, k_pages, v_pages, page_table, summaries, seq_lens, out, selected,
+                                   workspace, (hipStream_t)stream);
 }
 
 int se_quest_scores(const se_kv_layout* layout, const se_decode_params* params, const void* q, const void* k_pages,
@@ -328,6 +368,7 @@ int se_decode_selected(const se_kv_layout* layout, const se_decode_params* param
   if (rc) return rc;
   const bool dense = selected == nullptr;
   const DecodeWs w = decode_ws(layout, params, dense);
+  if (!w.fits) return SE_EUNSUPPORTED;
   if (!workspace || workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return SE_EWORKSPACE;
   char* ws = static_cast<char*>(workspace);
   se::DecodeArgs d;
@@ -347,6 +388,7 @@ int se_decode_selected(const se_kv_layout* layout, const se_decode_params* param
   d.topk = kept_cap(params);  // row length of the selection
   d.splits = w.splits;
   d.scale = eff_scale(layout, params);
+  d.valu = params->valu_attention != 0;
   return hip_status(se::launch_decode(to_layout(layout), d, (hipStream_t)stream));
 }
 

@@ -5,7 +5,21 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/se.h"
+
 namespace se {
+
+// se_sparse_decode in two halves.  sparse_decode_check runs every host-side
+// check of the arguments except the workspace and sets *need to the
+// workspace bytes the call takes (0 for an empty batch); sparse_decode_enqueue
+// launches the step with a workspace of at least that many bytes, 256-byte
+// aligned, on stream st (only after a successful check).
+int sparse_decode_check(const se_kv_layout* layout, const se_decode_params* params, const void* q,
+                        const void* k_pages, const void* v_pages, const int32_t* page_table, const void* summaries,
+                        const int32_t* seq_lens, const float* out, size_t* need);
+int sparse_decode_enqueue(const se_kv_layout* layout, const se_decode_params* params, const void* q,
+                          const void* k_pages, const void* v_pages, const int32_t* page_table, void* summaries,
+                          const int32_t* seq_lens, float* out, int32_t* selected, void* workspace, hipStream_t st);
 
 struct Layout {
   int hkv, dk, dv, visk;
@@ -49,8 +63,13 @@ struct DecodeArgs {
   float* part_ml;   // [B, Hq, S, 2]
   int B, Hq, MP, topk, splits;
   float scale;
+  bool valu;  // vector-ALU attention kernel for every shape
 };
-int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, int requested);
+// Split count of the attention over at most min(topk, MP) pages per (request,
+// KV head) (every page when dense); `requested` > 0 asks for that many.
+int decode_splits(const Layout& L, int B, int Hq, int MP, int topk, bool dense, int requested, bool valu);
+// Most pages one split of the chosen attention kernel can hold.
+int decode_max_pps(const Layout& L, int G, bool valu);
 size_t decode_partials_bytes(const Layout& L, int B, int Hq, int splits);
 hipError_t launch_decode(const Layout& L, const DecodeArgs& a, hipStream_t st);
 

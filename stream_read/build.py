@@ -1,16 +1,18 @@
 """Build libse_hbmread.so, the plain streaming-read kernel that bench.py
 measures the decode step against, in-tree with the library's hipcc flags.
+It is measurement equipment beside bench.py, not part of the library.
 
-Run as ``python -m sparse_kv_long_amd.probe.build`` or call ``build_probe()``.
+Run as ``python -m stream_read.build`` or call ``build_probe()``.
 """
 from __future__ import annotations
 
 import os
 import subprocess
 
-from sparse_kv_long_amd.build import ARCH, COMMON, HIPCC, HERE
+from sparse_kv_long_amd.build import ARCH, COMMON, HIPCC
 
-PROBE_SRC = os.path.join(HERE, "probe", "hbm_read.hip")
+HERE = os.path.dirname(os.path.abspath(__file__))
+PROBE_SRC = os.path.join(HERE, "hbm_read.hip")
 PROBE_LIB = os.path.join(HERE, "libse_hbmread.so")
 
 

@@ -49,23 +49,47 @@ def build_summaries(x, wl):
     return summ
 
 
-def params_for(wl, topk=None, refresh=1, splits=0, head_agg=0, sink=0, recent=0):
+def params_for(wl, topk=None, refresh=1, splits=0, head_agg=0, sink=0, recent=0, valu=0):
     return se.decode_params(wl.batch, wl.num_q_heads, wl.max_pages, wl.topk if topk is None else topk, wl.scale,
-                            head_agg, refresh, splits, sink, recent)
+                            head_agg, refresh, splits, sink, recent, valu)
+
+
+# Workspace fills: 0xFF bytes read as fp32 NaN and int32 -1, zeros as 0.0 and
+# 0.  Every call that takes a workspace runs once on each (call_twice), so a
+# kernel that reads workspace memory its own call did not write sees two
+# different values and the outputs differ.
+FILL_FIRST, FILL_SECOND = 0xFF, 0x00
 
 
 def workspace(nbytes):
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+    """A workspace buffer, filled with 0xFF bytes (NaN / -1)."""
+    return torch.full((max(nbytes, 256),), FILL_FIRST, dtype=torch.uint8, device=DEV)
 
 
-def run_sparse_decode(x, wl, summ, topk=None, refresh=1, splits=0, head_agg=0, sink=0, recent=0):
-    P = params_for(wl, topk, refresh, splits, head_agg, sink, recent)
+def call_twice(call, ws, outputs, what=""):
+    """Run call() on a workspace filled with 0xFF bytes, then again on the same
+    workspace filled with zeros; every tensor in `outputs` must come out
+    bitwise identical (the second call recomputes them from the same inputs)."""
+    ws.fill_(FILL_FIRST)
+    call()
+    torch.cuda.synchronize()
+    first = [o.clone() for o in outputs]
+    ws.fill_(FILL_SECOND)
+    call()
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(zip(first, outputs)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), \
+            f"{what}: output {i} depends on the workspace's prior contents"
+
+
+def run_sparse_decode(x, wl, summ, topk=None, refresh=1, splits=0, head_agg=0, sink=0, recent=0, valu=0):
+    P = params_for(wl, topk, refresh, splits, head_agg, sink, recent, valu)
     L = layout_for(wl)
     ws = workspace(se.se_sparse_decode_workspace_size(L, P))
     out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim_v), dtype=torch.float32, device=DEV)
     sel = torch.empty((wl.batch, wl.num_kv_heads, se.kept_capacity(P)), dtype=torch.int32, device=DEV)
-    se.se_sparse_decode(L, P, x["q"], x["k_pages"], x["v_pages"], x["page_table"], summ, x["seq_lens"], out, sel, ws)
-    torch.cuda.synchronize()
+    call_twice(lambda: se.se_sparse_decode(L, P, x["q"], x["k_pages"], x["v_pages"], x["page_table"], summ,
+                                           x["seq_lens"], out, sel, ws), ws, [out, sel], "se_sparse_decode")
     return out, sel
 
 

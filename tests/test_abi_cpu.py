@@ -29,7 +29,7 @@ def test_every_header_function_is_exported_and_wrapped(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert se.se_version() == 300
+    assert se.se_version() == 400
     assert se.se_status_string(0) == "ok"
     assert "invalid" in se.se_status_string(1)
     assert "unsupported" in se.se_status_string(2)
@@ -39,7 +39,7 @@ def test_version_and_status_strings(lib):
 
 def test_struct_sizes_match_header():
     assert ctypes.sizeof(se.KvLayout) == 6 * 4 + 3 * 8
-    assert ctypes.sizeof(se.DecodeParams) == 10 * 4
+    assert ctypes.sizeof(se.DecodeParams) == 11 * 4
     assert ctypes.sizeof(se.SnapKVParams) == 14 * 4
 
 
@@ -85,12 +85,31 @@ def test_workspace_size_query():
     (lambda L, P: setattr(P, "head_agg", 2), se.SE_EINVAL),
     (lambda L, P: setattr(P, "refresh_last_page", 3), se.SE_EINVAL),
     (lambda L, P: setattr(P, "num_splits", -2), se.SE_EINVAL),
+    (lambda L, P: setattr(P, "valu_attention", 2), se.SE_EINVAL),
 ])
 def test_decode_argument_errors(mutate, code):
     L = se.paged_layout(4, 128, 128)
     P = se.decode_params(2, 32, 64, 8)
     mutate(L, P)
     assert rc_decode(L, P) == code
+
+
+@pytest.mark.parametrize("valu", [0, 1])
+@pytest.mark.parametrize("dk,dv,visk,G", [(64, 64, False, 32), (64, 64, False, 16), (128, 128, False, 32),
+                                          (128, 128, False, 8), (128, 128, False, 16), (576, 512, True, 32)])
+@pytest.mark.parametrize("kcap", [1, 255, 32769, 65536, 3 * 65536])
+def test_every_split_fits_its_kernel(dk, dv, visk, G, kcap, valu):
+    """Any page budget the parameter checks accept gets a split count whose
+    splits each hold no more pages than the chosen attention kernel stages
+    (a budget of 40,000 pages at head dim 64 used to pass the checks and fail
+    at launch); the largest budgets, with forced pages on top, included."""
+    L = se.paged_layout(1, dk, dv, visk)
+    topk = min(kcap, 65536)
+    sink = min(kcap - topk, 65536)
+    recent = kcap - topk - sink
+    for MP in (kcap, 65536):
+        P = se.decode_params(2, G, min(MP, 65536), topk, sink_pages=sink, recent_pages=recent, valu_attention=valu)
+        assert se.se_sparse_decode_workspace_size(L, P) > 0
 
 
 @pytest.mark.parametrize("which", ["q", "k", "v", "pt", "lens", "out", "summ"])
@@ -235,7 +254,7 @@ def test_pyramid_budget_errors():
 def test_streaming_read_probe_loads_and_rejects_bad_arguments():
     """The streaming-read yardstick bench.py reports against is built beside
     the library and checks its arguments before it launches anything."""
-    from sparse_kv_long_amd.probe.build import PROBE_LIB
+    from stream_read.build import PROBE_LIB
     h = ctypes.CDLL(PROBE_LIB)
     f = h.se_hbm_read
     f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]

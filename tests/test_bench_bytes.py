@@ -15,7 +15,8 @@ def test_128k_workload_step_and_scorer_bytes():
     assert a["kv"] == 32 * 4 * 256 * 16 * 512 == 256 * 2 ** 20
     assert a["out"] == 32 * 32 * 128 * 4 == 512 * 1024
     assert a["step"] == 807_141_376  # 769.75 MiB
-    assert a["scorer_launch"] == 256 * 1024 + 512 * 2 ** 20 + 2 ** 20 + 32 * 4 * 8192 * 4 == 542_375_936
+    # q, summaries and page table; the page scores written are an intermediate
+    assert a["scorer_launch"] == 256 * 1024 + 512 * 2 ** 20 + 2 ** 20 == 538_181_632
 
 
 def test_32k_workload_step_bytes():
@@ -59,4 +60,4 @@ def test_snapkv_workload_bytes():
     first = 16 * 8 * 2081 * 512 + 16 * 32 * 128 * 6
     assert dec == sum(16 * 8 * (2081 + s) * 512 for s in range(64)) + 64 * 16 * 32 * 128 * 6
     assert dec > 64 * first
-    assert votes == q_win + k_once + 16 * 8 * 32768 * 4
+    assert votes == q_win + k_once  # the votes written are an intermediate

@@ -10,7 +10,7 @@ import torch
 import oracle
 import sparse_kv_long_amd as se
 from synth import SnapKVWorkload, make_snapkv_inputs, bf16_bits
-from gpu_util import DEV, announce, check_attention, check_selection, to_np, workspace
+from gpu_util import call_twice, DEV, announce, check_attention, check_selection, to_np, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -56,10 +56,10 @@ def run_evict(p, kcap, q_win, k, v, lens, positions=None):
     kept = torch.full((B, H, kcap), 777, dtype=torch.int32, device=DEV)
     klen = torch.zeros((B, H), dtype=torch.int32, device=DEV)
     if positions is None:
-        se.se_snapkv_compact(p, q_win, k, v, lens, k_out, v_out, kept, klen, ws)
+        call = lambda: se.se_snapkv_compact(p, q_win, k, v, lens, k_out, v_out, kept, klen, ws)
     else:
-        se.se_snapkv_recompact(p, q_win, k, v, lens, positions, k_out, v_out, kept, klen, ws)
-    torch.cuda.synchronize()
+        call = lambda: se.se_snapkv_recompact(p, q_win, k, v, lens, positions, k_out, v_out, kept, klen, ws)
+    call_twice(call, ws, [k_out, v_out, kept, klen], "eviction")
     return k_out, v_out, kept, klen
 
 
@@ -107,8 +107,7 @@ def test_h2o_votes_match_oracle():
     p, _ = params(wl, 0, 200, None)
     ws = workspace(se.se_snapkv_workspace_size(p))
     votes = torch.full((wl.batch, wl.num_kv_heads, wl.prompt), float("nan"), device=DEV)
-    se.se_snapkv_votes(p, x["q_win"], x["k"], x["prompt_lens"], votes, ws)
-    torch.cuda.synchronize()
+    call_twice(lambda: se.se_snapkv_votes(p, x["q_win"], x["k"], x["prompt_lens"], votes, ws), ws, [votes], "h2o votes")
     V = to_np(votes)
     qb, kb = bf16_bits(x["q_win"]), bf16_bits(x["k"])
     G = wl.group
@@ -223,8 +222,8 @@ def test_reeviction_after_decode_steps(case):
     pt = (torch.arange(B, device=DEV)[:, None] * (H * MP) + torch.arange(MP, device=DEV)[None]).to(torch.int32)
     out = torch.empty((B, wl.num_q_heads, D), dtype=torch.float32, device=DEV)
     dl = klen2[:, 0].to(torch.int32)
-    se.se_sparse_decode(Ld, Pd, x["q_steps"][S - 1], k2, v2, pt, None, dl, out, None, wsd)
-    torch.cuda.synchronize()
+    call_twice(lambda: se.se_sparse_decode(Ld, Pd, x["q_steps"][S - 1], k2, v2, pt, None, dl, out, None, wsd), wsd,
+               [out], "decode after re-eviction")
     o, qs = to_np(out), bf16_bits(x["q_steps"][S - 1])
     for b in range(B):
         ref = oracle.decode_over_rows(qs[b], ko2[b], vo2[b], int(dl[b]), G, wl.scale)

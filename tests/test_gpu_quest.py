@@ -113,10 +113,10 @@ def test_topk_pages_exact(MP, topk):
             assert (got[b, g, k:] == -1).all()
 
 
-def _decode_case(name, topk=None, splits=0):
+def _decode_case(name, topk=None, splits=0, valu=0):
     wl, x = make(name)
     summ = build_summaries(x, wl)
-    out, sel = run_sparse_decode(x, wl, summ, topk=topk, refresh=1, splits=splits)
+    out, sel = run_sparse_decode(x, wl, summ, topk=topk, refresh=1, splits=splits, valu=valu)
     h = host_inputs(x)
     ref_summ = oracle.quest_summaries(h["k"], h["pt"], h["lens"])
     A = oracle.quest_scores(h["q"], ref_summ, h["lens"], wl.group, wl.scale)
@@ -136,6 +136,38 @@ def test_sparse_decode_matches_oracle(name):
     wl, x, out, sel, ref = _decode_case(name)
     vmax = float(torch.nan_to_num(x["v_pages"] if x["v_pages"] is not None else x["k_pages"], 0.0).abs().max())
     check_attention(to_np(out), ref, vmax, name)
+
+
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("name", ["d128_g8", "d128_g16", "d128_g4_outlier", "d128_g1", "mla", "mla_g8", "d64_g4"])
+def test_valu_attention_matches_oracle(name, splits):
+    """valu_attention = 1: the vector-ALU attention kernel also on the shapes
+    that otherwise run on the matrix cores (head dim 128 with up to 16 query
+    heads per KV head, the 576/512 latent layout), with the automatic, one
+    and three splits."""
+    wl, x, out, sel, ref = _decode_case(name, splits=splits, valu=1)
+    vmax = float(torch.nan_to_num(x["v_pages"] if x["v_pages"] is not None else x["k_pages"], 0.0).abs().max())
+    check_attention(to_np(out), ref, vmax, f"{name} valu splits {splits}")
+
+
+def test_budget_beyond_a_thousand_splits():
+    """Head dim 64 with 32 query heads per KV head stages at most 16 pages per
+    split; 18,000 kept pages of 20,000 need 1,125 splits, more than the split
+    count could reach before (such a call used to pass the host checks and
+    fail at launch)."""
+    wl = QuestWorkload("t_many_splits", 1, 32, 1, 64, 64, 20000 * 16, 18000, "none", seed=24)
+    announce(f"many splits seed {wl.seed}")
+    x = make_quest_inputs(wl, DEV, poison_tail=True, seq_lens=[20000 * 16 - 3])
+    summ = build_summaries(x, wl)
+    out, sel = run_sparse_decode(x, wl, summ)
+    h = host_inputs(x)
+    ref_summ = oracle.quest_summaries(h["k"], h["pt"], h["lens"])
+    A = oracle.quest_scores(h["q"], ref_summ, h["lens"], wl.group, wl.scale)
+    sel_np = to_np(sel)
+    check_selection(sel_np[0, 0], A[0, 0, :20000], wl.topk, "many splits")
+    ref = oracle.sparse_attention(h["q"], h["k"], h["v"], h["pt"], h["lens"], sel_lists(sel_np, h["lens"]), wl.group,
+                                  wl.scale, wl.head_dim_v)
+    check_attention(to_np(out), ref, float(x["v_pages"].float().abs().max()), "many splits")
 
 
 def test_tiny_quest_workload_full_size():
@@ -171,8 +203,9 @@ def test_dense_mode_equals_full_attention(name):
     check_attention(to_np(out), ref, 8.0, name)
 
 
+@pytest.mark.parametrize("valu", [0, 1])
 @pytest.mark.parametrize("name", ["d128_g8", "mla", "d64_g4"])
-def test_split_count_invariance_and_determinism(name):
+def test_split_count_invariance_and_determinism(name, valu):
     wl, x = make(name)
     summ = build_summaries(x, wl)
     base = summ.clone()
@@ -181,7 +214,7 @@ def test_split_count_invariance_and_determinism(name):
     # LDS path (d128_g8 keeps 20 pages: 20 requested splits give 20)
     for splits in (1, 3, 16, 20, 0, 0):
         summ.copy_(base)
-        o, s = run_sparse_decode(x, wl, summ, splits=splits)
+        o, s = run_sparse_decode(x, wl, summ, splits=splits, valu=valu)
         outs.append((to_np(o), to_np(s)))
     # the matrix-core decode carries each attention weight as a hi + lo pair of
     # bf16 (|error| <= 2^-16 of the weight), so two summation orders may differ

@@ -7,7 +7,7 @@ import torch
 import oracle
 import sparse_kv_long_amd as se
 from synth import SnapKVWorkload, make_snapkv_inputs, bf16_bits
-from gpu_util import DEV, announce, check_attention, check_selection, to_np, workspace
+from gpu_util import call_twice, DEV, announce, check_attention, check_selection, to_np, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -52,8 +52,8 @@ def test_votes_match_oracle(name):
     p = params(wl)
     ws = workspace(se.se_snapkv_workspace_size(p))
     votes = torch.full((wl.batch, wl.num_kv_heads, wl.prompt), float("nan"), device=DEV)
-    se.se_snapkv_votes(p, x["q_win"], x["k"], x["prompt_lens"], votes, ws)
-    torch.cuda.synchronize()
+    call_twice(lambda: se.se_snapkv_votes(p, x["q_win"], x["k"], x["prompt_lens"], votes, ws), ws, [votes],
+               f"votes {name}")
     V = to_np(votes)
     h = host(x)
     for b, n in enumerate(h["lens"]):
@@ -102,8 +102,8 @@ def run_compact(wl, x):
     v_out = torch.zeros((B, H, C, D), dtype=torch.bfloat16, device=DEV)
     kept = torch.full((B, H, wl.budget + wl.window), 777, dtype=torch.int32, device=DEV)
     klen = torch.zeros((B, H), dtype=torch.int32, device=DEV)
-    se.se_snapkv_compact(p, x["q_win"], x["k"], x["v"], x["prompt_lens"], k_out, v_out, kept, klen, ws)
-    torch.cuda.synchronize()
+    call_twice(lambda: se.se_snapkv_compact(p, x["q_win"], x["k"], x["v"], x["prompt_lens"], k_out, v_out, kept, klen,
+                                            ws), ws, [k_out, v_out, kept, klen], f"compact {wl.name}")
     return k_out, v_out, kept, klen
 
 
@@ -150,8 +150,8 @@ def test_decode_over_compacted_cache(name):
         k_out[bi, :, rows] = x["k_steps"][s]
         v_out[bi, :, rows] = x["v_steps"][s]
         lens = (rows + 1).to(torch.int32)
-        se.se_sparse_decode(L, P, x["q_steps"][s], k_out, v_out, pt, None, lens, out, None, ws)
-        torch.cuda.synchronize()
+        call_twice(lambda: se.se_sparse_decode(L, P, x["q_steps"][s], k_out, v_out, pt, None, lens, out, None, ws), ws,
+                   [out], f"{name} step {s}")
         ko, vo, q = bf16_bits(k_out), bf16_bits(v_out), bf16_bits(x["q_steps"][s])
         o = to_np(out)
         for b in range(B):

@@ -16,7 +16,7 @@ MAGIC_I32 = 0x9E3779B9 - (1 << 32)  # the kernel's constant as a signed 32-bit w
 
 
 def _se_hbm_read():
-    from sparse_kv_long_amd.probe.build import PROBE_LIB
+    from stream_read.build import PROBE_LIB
     h = ctypes.CDLL(PROBE_LIB)
     f = h.se_hbm_read
     f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]

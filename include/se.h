@@ -196,6 +196,35 @@ int se_decode_selected(const se_kv_layout* layout, const se_decode_params* param
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * For callers that cannot allocate or pass a workspace: code under HIP graph
+ * capture that may not call hipMalloc, tight serving loops, harnesses that
+ * forbid allocation.
+ *
+ * se_sparse_decode_noalloc is se_sparse_decode (same arguments, same
+ * kernels, same results) with its workspace in a device array that the
+ * library holds: SE_NOALLOC_SCRATCH_BYTES on each GPU the call runs on, kept
+ * until the process ends.  It allocates nothing and calls no allocating
+ * routine.  The first call on a GPU looks the array's address up (that GPU
+ * must be the current device) and keeps it.
+ *   - The step must fit the array: se_sparse_decode_workspace_size of the
+ *     same layout and params must not exceed SE_NOALLOC_SCRATCH_BYTES, else
+ *     SE_EWORKSPACE.  (Batch 8 at 32K tokens with 8 KV heads takes 1.6 MiB,
+ *     batch 32 at 128K with 4 KV heads 20.5 MiB, 16 latent-attention
+ *     requests of up to 128K tokens 16.6 MiB.)
+ *   - `stream` must belong to the current device (SE_EINVAL otherwise);
+ *     SE_EHIP if the array's address cannot be obtained.
+ *   - Every call on one GPU uses the same array, and the array keeps what the
+ *     last call left (no call needs it cleared).  Calls that may overlap on
+ *     one GPU -- different streams without ordering between them -- race on
+ *     it: the caller must order them.
+ * ------------------------------------------------------------------------- */
+#define SE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+int se_sparse_decode_noalloc(const se_kv_layout* layout, const se_decode_params* params, const void* q,
+                             const void* k_pages, const void* v_pages, const int32_t* page_table, void* summaries,
+                             const int32_t* seq_lens, float* out, int32_t* selected, void* stream);
+
+/* ---------------------------------------------------------------------------
  * SnapKV eviction and compaction, and the eviction family around it.
  *
  * Per request b (prompt length n = prompt_lens[b]) and KV head g, with

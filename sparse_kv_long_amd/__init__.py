@@ -69,6 +69,7 @@ _SIG = {
     "se_quest_scores": ([_P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "se_topk_pages": ([_P, _I, _P, _P, _P, _P], ctypes.c_int),
     "se_decode_selected": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
+    "se_sparse_decode_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], ctypes.c_int),
     "se_snapkv_workspace_size": ([_P, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
     "se_snapkv_compact": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
     "se_snapkv_votes": ([_P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P], ctypes.c_int),
@@ -191,6 +192,16 @@ def se_sparse_decode(layout, params, q, k_pages, v_pages, page_table, summaries,
     _check(lib().se_sparse_decode(ctypes.byref(layout), ctypes.byref(params), _ptr(q), _ptr(k_pages), _ptr(v_pages),
                                   _ptr(page_table), _ptr(summaries), _ptr(seq_lens), _ptr(out), _ptr(selected),
                                   _ptr(workspace), _nbytes(workspace), _stream(stream)), "se_sparse_decode")
+
+
+def se_sparse_decode_noalloc(layout, params, q, k_pages, v_pages, page_table, summaries, seq_lens, out, selected,
+                             stream=None):
+    _check(lib().se_sparse_decode_noalloc(ctypes.byref(layout), ctypes.byref(params), _ptr(q), _ptr(k_pages),
+                                          _ptr(v_pages), _ptr(page_table), _ptr(summaries), _ptr(seq_lens), _ptr(out),
+                                          _ptr(selected), _stream(stream)), "se_sparse_decode_noalloc")
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # SE_NOALLOC_SCRATCH_BYTES
 
 
 def se_quest_scores(layout, params, q, k_pages, page_table, summaries, seq_lens, scores, stream=None):

@@ -112,6 +112,23 @@ def test_every_split_fits_its_kernel(dk, dv, visk, G, kcap, valu):
         assert se.se_sparse_decode_workspace_size(L, P) > 0
 
 
+def test_noalloc_refuses_steps_beyond_its_array_before_any_launch():
+    """se_sparse_decode_noalloc checks its arguments as se_sparse_decode does,
+    and refuses a step whose workspace exceeds SE_NOALLOC_SCRATCH_BYTES
+    (a 65536-page table for 32 requests and 4 KV heads: 32 MiB of scores
+    alone) before anything is enqueued."""
+    L = se.paged_layout(4, 128, 128)
+    big = se.decode_params(32, 32, 65536, 256)
+    assert se.se_sparse_decode_workspace_size(L, big) > se.NOALLOC_SCRATCH_BYTES
+    f = se.lib().se_sparse_decode_noalloc
+    assert f(ctypes.byref(L), ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == \
+        se.SE_EWORKSPACE
+    bad = se.decode_params(2, 32, 64, 8, head_agg=5)
+    assert f(ctypes.byref(L), ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == se.SE_EINVAL
+    ok = se.decode_params(2, 32, 64, 8)
+    assert f(ctypes.byref(L), ctypes.byref(ok), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == se.SE_EINVAL
+
+
 @pytest.mark.parametrize("which", ["q", "k", "v", "pt", "lens", "out", "summ"])
 def test_decode_null_pointers(which):
     L = se.paged_layout(4, 128, 128)

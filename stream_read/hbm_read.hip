@@ -1,5 +1,5 @@
 // A plain streaming read, the yardstick for the decode step's effective
-// bandwidth: each block reads its own contiguous share of the buffer in
+// bandwidth (and, with ordinary loads, a re-read of a cache-sized buffer): each block reads its own contiguous share of the buffer in
 // order, every lane 16 bytes per load, four loads in flight, non-temporal, and
 // keeps only an XOR of the words it read (stored in the one case it equals a
 // fixed constant, so the loads stay).  A contiguous share per block streams faster
@@ -19,6 +19,16 @@ constexpr uint32_t kNeverSeen = 0x9e3779b9u;
 
 __device__ __forceinline__ uint32_t fold(u32x4 v) { return v.x ^ v.y ^ v.z ^ v.w; }
 
+// NT: non-temporal loads (a buffer read once); else ordinary loads, which
+// the caches keep, so a buffer small enough for the 256 MB Infinity Cache is
+// served from it when read again.
+template <bool NT>
+__device__ __forceinline__ u32x4 load(const u32x4* p) {
+  if (NT) return __builtin_nontemporal_load(p);
+  return *p;
+}
+
+template <bool NT>
 __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const u32x4* __restrict__ p, int64_t n16,
                                                             uint32_t* __restrict__ out) {
   const int64_t share = (n16 + gridDim.x - 1) / gridDim.x;
@@ -26,13 +36,13 @@ __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const u32x4* __restr
   int64_t i = (int64_t)blockIdx.x * share + threadIdx.x;
   uint32_t acc = 0;
   for (; i + 3 * kThreads < end; i += 4 * kThreads) {
-    const u32x4 a = __builtin_nontemporal_load(p + i);
-    const u32x4 b = __builtin_nontemporal_load(p + i + kThreads);
-    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * kThreads);
-    const u32x4 d = __builtin_nontemporal_load(p + i + 3 * kThreads);
+    const u32x4 a = load<NT>(p + i);
+    const u32x4 b = load<NT>(p + i + kThreads);
+    const u32x4 c = load<NT>(p + i + 2 * kThreads);
+    const u32x4 d = load<NT>(p + i + 3 * kThreads);
     acc ^= fold(a) ^ fold(b) ^ fold(c) ^ fold(d);
   }
-  for (; i < end; i += kThreads) acc ^= fold(__builtin_nontemporal_load(p + i));
+  for (; i < end; i += kThreads) acc ^= fold(load<NT>(p + i));
   if (acc == kNeverSeen) out[0] = acc;
 }
 
@@ -45,7 +55,17 @@ __global__ __launch_bounds__(kThreads) void hbm_read_kernel(const u32x4* __restr
 // HIP error of the launch.
 extern "C" int se_hbm_read(const void* buf, int64_t bytes, int blocks, uint32_t* out, hipStream_t stream) {
   if (!buf || !out || bytes <= 0 || bytes % 16 != 0 || blocks < 1 || blocks > 65536) return -1;
-  hipLaunchKernelGGL(hbm_read_kernel, dim3(blocks), dim3(kThreads), 0, stream, static_cast<const u32x4*>(buf),
+  hipLaunchKernelGGL(hbm_read_kernel<true>, dim3(blocks), dim3(kThreads), 0, stream, static_cast<const u32x4*>(buf),
+                     bytes / 16, out);
+  return static_cast<int>(hipGetLastError());
+}
+
+// The same read with ordinary loads: called again on a buffer that fits the
+// Infinity Cache it measures the rate at which the cache feeds the compute
+// dies.  Same arguments and errors as se_hbm_read.
+extern "C" int se_cache_reread(const void* buf, int64_t bytes, int blocks, uint32_t* out, hipStream_t stream) {
+  if (!buf || !out || bytes <= 0 || bytes % 16 != 0 || blocks < 1 || blocks > 65536) return -1;
+  hipLaunchKernelGGL(hbm_read_kernel<false>, dim3(blocks), dim3(kThreads), 0, stream, static_cast<const u32x4*>(buf),
                      bytes / 16, out);
   return static_cast<int>(hipGetLastError());
 }

@@ -273,13 +273,14 @@ def test_streaming_read_probe_loads_and_rejects_bad_arguments():
     the library and checks its arguments before it launches anything."""
     from stream_read.build import PROBE_LIB
     h = ctypes.CDLL(PROBE_LIB)
-    f = h.se_hbm_read
-    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    f.restype = ctypes.c_int
-    good = ctypes.c_void_p(0x1000)
-    assert f(None, 16, 1, good, None) == -1
-    assert f(good, 16, 1, None, None) == -1
-    assert f(good, 0, 1, good, None) == -1
-    assert f(good, 24, 1, good, None) == -1  # not a multiple of 16
-    assert f(good, 16, 0, good, None) == -1
-    assert f(good, 16, 65537, good, None) == -1
+    for name in ("se_hbm_read", "se_cache_reread"):
+        f = getattr(h, name)
+        f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        f.restype = ctypes.c_int
+        good = ctypes.c_void_p(0x1000)
+        assert f(None, 16, 1, good, None) == -1
+        assert f(good, 16, 1, None, None) == -1
+        assert f(good, 0, 1, good, None) == -1
+        assert f(good, 24, 1, good, None) == -1  # not a multiple of 16
+        assert f(good, 16, 0, good, None) == -1
+        assert f(good, 16, 65537, good, None) == -1

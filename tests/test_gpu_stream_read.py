@@ -1,8 +1,9 @@
-"""The streaming-read yardstick that bench.py reports the decode step against
-reads every 16-byte chunk of its buffer: each lane folds what it reads into
-one XOR and stores only if that equals a fixed constant, so a zero buffer with
-one planted chunk that folds to the constant is stored from, wherever the
-chunk sits and whatever the grid, only if that chunk is read."""
+"""The streaming-read yardstick that bench.py reports the decode step against,
+and its cache re-read twin, read every 16-byte chunk of their buffer: each
+lane folds what it reads into one XOR and stores only if that equals a fixed
+constant, so a zero buffer with one planted chunk that folds to the constant
+is stored from, wherever the chunk sits and whatever the grid, only if that
+chunk is read."""
 import ctypes
 
 import pytest
@@ -15,20 +16,21 @@ pytestmark = pytest.mark.gpu
 MAGIC_I32 = 0x9E3779B9 - (1 << 32)  # the kernel's constant as a signed 32-bit word
 
 
-def _se_hbm_read():
+def _read_fn(name):
     from stream_read.build import PROBE_LIB
     h = ctypes.CDLL(PROBE_LIB)
-    f = h.se_hbm_read
+    f = getattr(h, name)
     f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     f.restype = ctypes.c_int
     return f
 
 
+@pytest.mark.parametrize("name", ["se_hbm_read", "se_cache_reread"])
 @pytest.mark.parametrize("blocks", [1, 7, 1024, 65536])
 @pytest.mark.parametrize("nbytes", [16, 4096 + 48, (3 << 20) + 16 * 5])
-def test_every_chunk_is_read(blocks, nbytes):
-    announce(f"se_hbm_read {nbytes} B, {blocks} blocks")
-    f = _se_hbm_read()
+def test_every_chunk_is_read(name, blocks, nbytes):
+    announce(f"{name} {nbytes} B, {blocks} blocks")
+    f = _read_fn(name)
     nchunk = nbytes // 16
     g = torch.Generator()
     g.manual_seed(nbytes * 131 + blocks)

@@ -17,6 +17,9 @@ SMALL = {
     "d128_g32_w8": (SnapKVWorkload("s_g32", 1, 32, 1, 128, 500, 8, 7, 64, 2, seed=33), [500]),
     "d128_g1_w1": (SnapKVWorkload("s_w1", 2, 2, 2, 128, 400, 1, 5, 50, 2, seed=34), [400, 333]),
     "d128_g8_w24": (SnapKVWorkload("s_g8", 1, 8, 1, 128, 800, 24, 9, 200, 2, seed=35), [800]),
+    # 16 heads x 128 window rows = 2048 rows: sixteen row groups, more than a
+    # block's waves can take, so each row group gets blocks of its own
+    "d64_g16_w128": (SnapKVWorkload("s_rows", 2, 16, 1, 64, 400, 128, 5, 60, 2, seed=37), [400, 250]),
     # empty prompt, shorter than the window, exactly the window, prefix == budget (identity),
     # prefix one past the budget, and a long one
     "edges": (SnapKVWorkload("s_edge", 6, 8, 2, 128, 300, 16, 5, 40, 2, seed=36), [0, 7, 16, 56, 57, 300]),

@@ -156,7 +156,7 @@ def test_snapkv_full_size_every_unit():
 
 
 @pytest.mark.parametrize("name", ["h2o", "prune", "pyramid_layer0", "pyramid_layer3"])
-def test_eviction_family_full_size_sampled_units(name):
+def test_eviction_family_full_size_every_unit(name):
     """The H2O, prefix-pruning and PyramidKV legs at the size the bench runs
     (PyramidKV: its first and last layers' budgets): counts, forced tokens,
     bitwise copies, and votes and selection against the oracle, on every unit."""

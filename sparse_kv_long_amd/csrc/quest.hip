@@ -293,7 +293,7 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
     constexpr int CPR = NCH / 8;  // chunks per lane per record
     uint4* tile = stage_lds + wave * 16 * NCH;
     const int r8 = lane >> 3, j8 = lane & 7;
-    uint4 dA[2][CPR], dB[2][CPR];
+    uint4 dA[2][CPR];
     auto load = [&](int t, uint4 (&d)[2][CPR]) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -323,27 +323,13 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
       __builtin_amdgcn_wave_barrier();
       finish(acc, start + 16 * t, end);
     };
-    // two tiles per step while a third follows, then the one or two left
-    // without prefetch: every tile is fetched once (a clamped prefetch past
-    // the last tile re-fetched it, the loads being non-temporal), and inside
-    // the loop the loads stay unconditional, so the compiler waits for one
-    // tile at a time instead of draining both
-    load(0, dA);
-    int t = 0;
-    for (; t + 2 < ntile; t += 2) {
-      load(t + 1, dB);
-      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-      score(t, dA);
-      load(t + 2, dA);
-      __builtin_amdgcn_sched_barrier(0);
-      score(t + 1, dB);
-    }
-    if (t + 1 < ntile) {
-      load(t + 1, dB);
-      __builtin_amdgcn_sched_barrier(0);
-      score(t, dA);
-      score(t + 1, dB);
-    } else {
+    // one tile at a time, no prefetch: while a wave waits for its tile the
+    // CU's other eleven waves keep HBM busy.  A tile in flight per wave on
+    // top of that made the bare loads of this random 512-byte-record stream
+    // slower (3,072 waves: 88 against 84.5 us); the scorer itself measured
+    // the same at 128K and 19.2 against 20.6 us at 32K (events)
+    for (int t = 0; t < ntile; ++t) {
+      load(t, dA);
       score(t, dA);
     }
   }

@@ -65,3 +65,44 @@ def test_noalloc_rejects_a_step_beyond_the_array():
     rc = se.lib().se_sparse_decode_noalloc(ctypes.byref(L), ctypes.byref(P), p, p, p, p, p, p, p, None,
                                            torch.cuda.current_stream().cuda_stream)
     assert rc == se.SE_EWORKSPACE
+
+
+def test_noalloc_under_graph_capture():
+    """The callers the entry point is for: a captured se_sparse_decode_noalloc,
+    replayed with fresh queries and eager work in between, reproduces the
+    eager call bit for bit on every replay."""
+    wl = QuestWorkload("t_noalloc_graph", 3, 16, 2, 128, 128, 1500, 12, "zipf", seed=63)
+    announce("no-alloc graph capture")
+    x = make_quest_inputs(wl, DEV, seq_lens=[1500, 777, 33])
+    summ = build_summaries(x, wl)
+    L, P = layout_for(wl), params_for(wl, refresh=0)
+    q = x["q"].clone()
+    out = torch.empty((wl.batch, wl.num_q_heads, wl.head_dim_v), dtype=torch.float32, device=DEV)
+    sel = torch.empty((wl.batch, wl.num_kv_heads, wl.topk), dtype=torch.int32, device=DEV)
+
+    def call():
+        se.se_sparse_decode_noalloc(L, P, q, x["k_pages"], x["v_pages"], x["page_table"], summ, x["seq_lens"], out,
+                                    sel)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # the first call on this GPU looks up the array's address, outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call()
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(9)
+    for rep in range(4):
+        q.copy_(torch.randn(q.shape, generator=gen, device=DEV).to(torch.bfloat16))
+        call()  # eager
+        torch.cuda.synchronize()
+        want_out, want_sel = out.clone(), sel.clone()
+        out.fill_(float("nan"))
+        sel.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want_out), f"replay {rep}: output differs from the eager call"
+        assert torch.equal(sel, want_sel), f"replay {rep}: selection differs from the eager call"

@@ -343,7 +343,8 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
 // sequence (unit-major); block i takes the i-th of gridDim.x equal shares, as
 // segments of one or more units, so a ragged batch keeps every block equally
 // busy.  The last page of each unit, whose summary is rebuilt first, is
-// handled by block (unit mod gridDim.x) after its share.
+// handled by block (unit mod gridDim.x) before its share, which is shortened
+// by kRefreshPages pages per rebuild so that those blocks finish with the rest.
 //
 // Within a segment the block streams 16-page tiles: its threads fetch a
 // tile's records as contiguous runs (consecutive threads take consecutive
@@ -359,6 +360,11 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
 constexpr int kWideChunk = 1024;     // page ids staged per pass over a segment
 constexpr int kWideWaves = 4;
 constexpr int kWideMaxUnits = 2048;  // units per launch (prefix sums live in LDS)
+// A last-page rebuild and score counted as this many pages of a block's share
+// (MLA ragged batch: the scorer took 46.4 us with the rebuilds after the
+// shares, 45.8 / 45.4 / 44.9 us with them first at 16 / 32 / 48 pages, and
+// 44.9 us with no rebuild at all)
+constexpr int kRefreshPages = 48;
 
 template <int D, int NT, int RD, int NW>
 __global__ __launch_bounds__(NW * 64)
@@ -406,7 +412,21 @@ void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs
   }
   __syncthreads();
   const int64_t total = pre[nunits];
-  const int64_t lo = total * blockIdx.x / gridDim.x, hi = total * (blockIdx.x + 1) / gridDim.x;
+  // Block i rebuilds and scores the last pages of units i, i + gridDim.x, ...
+  // first (when refreshing), and that chain counts as kRefreshPages pages of
+  // its share: the blocks' page ranges are cut from total + kRefreshPages *
+  // nunits virtual pages, each refresh taken out of its block's range, so the
+  // refreshing blocks finish with the others.  Ranges stay consecutive
+  // (hi of block i is lo of block i + 1), so every page is scored; where the
+  // rounding makes neighbours overlap, a page is scored twice with the same
+  // result.
+  auto cut = [&](int i) -> int64_t {
+    if (!a.refresh) return total * i / gridDim.x;
+    const int64_t nr = (int64_t)i * (nunits / gridDim.x) + min(i, nunits % (int)gridDim.x);  // refreshes of blocks < i
+    const int64_t v = (total + (int64_t)kRefreshPages * nunits) * i / gridDim.x - (int64_t)kRefreshPages * nr;
+    return v < 0 ? 0 : v > total ? total : v;
+  };
+  const int64_t lo = cut(blockIdx.x), hi = max(lo, cut(blockIdx.x + 1));
 
   // partial tiles -> KV-head scores of pages base + 4*kq + wave (waves 0..3,
   // lanes col == 0 store)
@@ -448,6 +468,43 @@ void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs
   };
 
   int buf = 0;
+  // ---- last pages first: rebuild each summary from its valid keys, store it, score it
+  for (int ur = blockIdx.x; a.refresh && ur < nunits; ur += gridDim.x) {
+    const int b = (u0 + ur) / Hkv, g = (u0 + ur) % Hkv;
+    const int n = a.seq_lens[b];
+    const int P = (n + kPage - 1) / kPage;
+    if (P == 0) continue;
+    const int plast = P - 1;
+    const int64_t pid = a.page_table[(int64_t)b * a.MP + plast];
+    const int valid = n - plast * kPage;
+    const int dc = D / 8;
+    uint16_t* rec = a.summ + (pid * Hkv + g) * 2 * D;
+    __syncthreads();  // rrec of the previous unit is no longer read
+    for (int ci = threadIdx.x; ci < NCH; ci += NTH) {
+      uint4 mn, mx;
+      minmax8(a.k + pid * ps + (int64_t)g * hs + 8 * (ci < dc ? ci : ci - dc), ts, valid, mn, mx);
+      const uint4 v = ci < dc ? mn : mx;
+      *reinterpret_cast<uint4*>(rec + 8 * ci) = v;
+      rrec[ci] = v;
+    }
+    __syncthreads();
+    if (a.topk < P) {
+      load_q(b, g);
+      f32x4_t sc[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        sc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KW; ++ks) {
+          const uint4 d = col == 0 ? rrec[kq + 4 * (KW * wave + ks)] : make_uint4(0, 0, 0, 0);
+          sc[nt] = mfma16(d, qb[nt][ks], sc[nt]);
+        }
+      }
+      finish(sc, buf, a.scores + ((int64_t)b * Hkv + g) * a.MP, plast, plast + 1);  // page slot 0 is the last page
+      buf ^= 1;
+    }
+  }
+
   // ---- this block's share, unit by unit ---------------------------------------
   int u = 0;
   while (u < nunits && pre[u + 1] <= lo) ++u;
@@ -522,43 +579,6 @@ void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs
     }
   }
 
-  // ---- last pages: rebuild each summary from its valid keys, store it, score it
-  if (!a.refresh) return;
-  for (int ur = blockIdx.x; ur < nunits; ur += gridDim.x) {
-    const int b = (u0 + ur) / Hkv, g = (u0 + ur) % Hkv;
-    const int n = a.seq_lens[b];
-    const int P = (n + kPage - 1) / kPage;
-    if (P == 0) continue;
-    const int plast = P - 1;
-    const int64_t pid = a.page_table[(int64_t)b * a.MP + plast];
-    const int valid = n - plast * kPage;
-    const int dc = D / 8;
-    uint16_t* rec = a.summ + (pid * Hkv + g) * 2 * D;
-    __syncthreads();  // rrec of the previous unit is no longer read
-    for (int ci = threadIdx.x; ci < NCH; ci += NTH) {
-      uint4 mn, mx;
-      minmax8(a.k + pid * ps + (int64_t)g * hs + 8 * (ci < dc ? ci : ci - dc), ts, valid, mn, mx);
-      const uint4 v = ci < dc ? mn : mx;
-      *reinterpret_cast<uint4*>(rec + 8 * ci) = v;
-      rrec[ci] = v;
-    }
-    __syncthreads();
-    if (a.topk < P) {
-      load_q(b, g);
-      f32x4_t sc[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        sc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KW; ++ks) {
-          const uint4 d = col == 0 ? rrec[kq + 4 * (KW * wave + ks)] : make_uint4(0, 0, 0, 0);
-          sc[nt] = mfma16(d, qb[nt][ks], sc[nt]);
-        }
-      }
-      finish(sc, buf, a.scores + ((int64_t)b * Hkv + g) * a.MP, plast, plast + 1);  // page slot 0 is the last page
-      buf ^= 1;
-    }
-  }
 }
 
 static int pick_ppw(int B, int Hkv, int MP) {

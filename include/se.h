@@ -260,7 +260,9 @@ typedef struct se_snapkv_params {
   int32_t num_q_heads;     /* Hq, a multiple of num_kv_heads, G <= 32         */
   int32_t num_kv_heads;    /* Hkv                                            */
   int32_t head_dim;        /* D; 128 or 64                                   */
-  int32_t max_prompt_len;  /* token dim of k, v: [B, Hkv, max_prompt_len, D] */
+  int32_t max_prompt_len;  /* token dim of k, v: [B, Hkv, max_prompt_len, D];
+                              max_prompt_len - window <= 65536 (longer:
+                              SE_EUNSUPPORTED)                             */
   int32_t window;          /* W, 1..128                                       */
   int32_t pool_kernel;     /* odd, 1 .. 129 (wider: SE_EUNSUPPORTED)          */
   int32_t budget;          /* R >= 1 candidates kept                          */

@@ -182,6 +182,7 @@ def test_decode_misaligned_and_workspace():
     (lambda p: setattr(p, "num_q_heads", 9), se.SE_EINVAL),
     (lambda p: setattr(p, "num_q_heads", 2 * 33), se.SE_EUNSUPPORTED),
     (lambda p: setattr(p, "max_prompt_len", 70000), se.SE_EUNSUPPORTED),
+    (lambda p: setattr(p, "max_prompt_len", 65536 + 32 + 1), se.SE_EUNSUPPORTED),  # prefix one past 65,536
 ])
 def test_snapkv_argument_errors(mutate, code):
     p = se.snapkv_params(2, 8, 2, 128, 1000, 32, 7, 64, 96)
@@ -189,6 +190,12 @@ def test_snapkv_argument_errors(mutate, code):
     rc = se.lib().se_snapkv_compact(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, OUT1, OUT2, FAKE, FAKE, FAKE, 1 << 40,
                                     None)
     assert rc == code
+
+
+def test_snapkv_longest_prompt_is_accepted():
+    # a 65,536-token prefix before the window is the longest the library takes
+    p = se.snapkv_params(2, 8, 2, 128, 65536 + 32, 32, 7, 64, 96)
+    assert se.se_snapkv_workspace_size(p) > 0
 
 
 def test_snapkv_pointer_and_workspace_errors():

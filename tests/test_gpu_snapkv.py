@@ -160,3 +160,32 @@ def test_decode_over_compacted_cache(name):
         for b in range(B):
             ref = oracle.decode_over_rows(q[b], ko[b], vo[b], int(lens[b]), wl.group, wl.scale)
             check_attention(o[b], ref, 8.0, f"{name} step {s} b{b}")
+
+
+def test_longest_prompt_selection_and_copies():
+    """The longest prompt the library takes (a 65,536-token prefix before the
+    32-token window): the kept positions of one (request, KV head) against
+    the oracle's pooled votes, and the kept rows copied bit for bit."""
+    n = 65536 + 32
+    wl = SnapKVWorkload("s_long", 1, 4, 1, 128, n, 32, 7, 2048, 1, seed=38)
+    x = make_snapkv_inputs(wl, DEV, prompt_lens=[n])
+    announce(f"snapkv longest prompt seed {wl.seed}")
+    p = params(wl)
+    ws = workspace(se.se_snapkv_workspace_size(p))
+    kcap = wl.budget + wl.window
+    k_out = torch.zeros((1, 1, wl.out_capacity, wl.head_dim), dtype=torch.bfloat16, device=DEV)
+    v_out = torch.zeros_like(k_out)
+    kept = torch.full((1, 1, kcap), 777, dtype=torch.int32, device=DEV)
+    klen = torch.zeros((1, 1), dtype=torch.int32, device=DEV)
+    call_twice(lambda: se.se_snapkv_compact(p, x["q_win"], x["k"], x["v"], x["prompt_lens"], k_out, v_out, kept, klen,
+                                            ws), ws, [k_out, v_out, kept, klen], "longest prompt")
+    n, Lp = wl.prompt, wl.prompt - wl.window
+    K = to_np(kept)[0, 0]
+    assert int(to_np(klen)[0, 0]) == kcap
+    assert (K[wl.budget:] == np.arange(Lp, n)).all()
+    h = host(x)
+    S = oracle_votes(h, wl, 0, 0)
+    check_selection(K[:wl.budget], oracle.maxpool1d(S, wl.pool_kernel), wl.budget, "longest prompt")
+    for src, dst in ((x["k"], k_out), (x["v"], v_out)):
+        want = src[0, 0, torch.from_numpy(K).long().to(DEV)]
+        assert torch.equal(want.view(torch.int16), dst[0, 0, :kcap].view(torch.int16))

@@ -346,48 +346,54 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
 // handled by block (unit mod gridDim.x) before its share, which is shortened
 // by kRefreshPages pages per rebuild so that those blocks finish with the rest.
 //
-// Within a segment the block streams 16-page tiles: its threads fetch a
-// tile's records as contiguous runs (consecutive threads take consecutive
-// 16-byte chunks of a record) into registers, RD tiles deep, and write the
-// current one to an LDS tile with chunk c of page p stored at slot c ^ (p & 7).
-// The NW waves split the tile's k dimension (wave w: k-steps KW*w .. KW*w +
-// KW-1), reading their A fragments from LDS without bank conflicts and keeping
-// their q+/q- fragments in registers.  The partial tiles are summed through
-// LDS in a fixed order and waves 0..3 finish rows i = w (pages 4*kq + w of the
-// tile).  Four waves of nine k-steps each, one block per CU: measured faster
-// than twelve or six waves of fewer k-steps, and than deeper rings.
+// A block has two waves; wave w owns query heads 16w .. 16w + 15 of the KV
+// head, with q of those heads for all 576 channels in registers (its
+// non-positive and non-negative parts are split off per k-step).  A 16-page
+// tile is fetched in two steps of eight pages; in each step a wave reads four
+// whole records (9 loads of 16 bytes per lane, consecutive lanes on
+// consecutive chunks) and writes them to the block's LDS tile, chunk c of page
+// p at slot c ^ (p & 7).  The next tile's first step is issued before the
+// current tile's matrix-core work, so each wave keeps one group of four
+// records in flight almost all the time.  Each wave then forms its 16 heads x
+// 16 pages of bounds over the whole contraction (A = q parts, B = the tile;
+// four accumulators summed in a fixed order), scales them, reduces over its
+// heads in registers and across the four lane rows, and wave 1 posts its
+// per-page value to LDS; after the next barrier wave 0 adds (or takes the max
+// of) both and stores the 16 scores.  No partial sums cross waves, and a tile
+// costs two block barriers.
+//
+// Measured on the MLA ragged batch (events): 42.1 us at two blocks per CU,
+// 46.8 at three and 48.0 at four (more records in flight made this random
+// record stream slower, not faster), 57.6 at one; 44.0 without the one-step
+// prefetch, 44.2 with both steps prefetched.  The block-cooperative form it
+// replaced (four waves splitting the k dimension, partial tiles summed
+// through LDS, a three-tile register ring) took 45.0 us, and 42-43 us with
+// its records served from the L2 instead of HBM: its time was set by its
+// per-tile chain of barriers and cross-wave sums, not by the memory.
 // ---------------------------------------------------------------------------
-constexpr int kWideChunk = 1024;     // page ids staged per pass over a segment
-constexpr int kWideWaves = 4;
-constexpr int kWideMaxUnits = 2048;  // units per launch (prefix sums live in LDS)
 // A last-page rebuild and score counted as this many pages of a block's share
-// (MLA ragged batch: the scorer took 46.4 us with the rebuilds after the
-// shares, 45.8 / 45.4 / 44.9 us with them first at 16 / 32 / 48 pages, and
-// 44.9 us with no rebuild at all)
+// (measured with the block-cooperative form: 46.4 us with the rebuilds after
+// the shares, 45.8 / 45.4 / 44.9 us with them first at 16 / 32 / 48 pages,
+// and 44.9 us with no rebuild at all)
 constexpr int kRefreshPages = 48;
+constexpr int kWideUnits = 256;       // units per launch (prefix sums live in LDS)
+constexpr int kWideBlocksPerCU = 2;   // one wave per SIMD: more waves in flight made this record stream slower
 
-template <int D, int NT, int RD, int NW>
-__global__ __launch_bounds__(NW * 64)
-void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs, int64_t ts, int u0, int nunits) {
-  constexpr int NTH = NW * 64;
-  constexpr int KS = 2 * D / 32;  // k steps per tile
-  constexpr int KW = KS / NW;     // k steps per wave
-  constexpr int NCH = D / 4;      // 16-byte chunks per record
-  constexpr int CPT = 16 * NCH / NTH;  // chunks per thread per tile
-  static_assert(KS % NW == 0 && (16 * NCH) % NTH == 0 && NCH % 8 == 0, "unsupported record width");
-  __shared__ int32_t ids[kWideChunk];
-  __shared__ uint4 tile[16 * NCH];
-  __shared__ f32x4_t part[2][NW][NT][kWave];
-  __shared__ uint4 rrec[NCH];
-  __shared__ int64_t pre[kWideMaxUnits + 1];  // pages to score before each unit
+template <int D, bool SUM>
+__global__ __launch_bounds__(128) void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs,
+                                                                int64_t ts, int u0, int nunits) {
+  constexpr int KS = 2 * D / 32;     // k steps per tile
+  constexpr int NCH = D / 4;         // 16-byte chunks per record
+  constexpr int CPL = 4 * NCH / 64;  // loads per lane per step (four whole records per wave)
+  static_assert((4 * NCH) % 64 == 0 && NCH % 8 == 0 && KS % 4 == 0, "unsupported record width");
+  __shared__ uint4 tile[16 * NCH];  // slots 0 .. NCH-1 also hold a rebuilt record while it is scored
+  __shared__ float agg[16];
+  __shared__ int64_t pre[kWideUnits + 1];
 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
-  const bool SUM = a.head_sum != 0;
   const int64_t pid_stride = (int64_t)Hkv * 2 * D;
 
-  // pages to score per unit (dense units score none; the refreshed last page
-  // is scored separately) and their prefix sums, by the first wave
   auto scored = [&](int u) -> int {
     const int b = (u0 + u) / Hkv;
     const int P = (a.seq_lens[b] + kPage - 1) / kPage;
@@ -412,62 +418,63 @@ void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs
   }
   __syncthreads();
   const int64_t total = pre[nunits];
-  // Block i rebuilds and scores the last pages of units i, i + gridDim.x, ...
-  // first (when refreshing), and that chain counts as kRefreshPages pages of
-  // its share: the blocks' page ranges are cut from total + kRefreshPages *
-  // nunits virtual pages, each refresh taken out of its block's range, so the
-  // refreshing blocks finish with the others.  Ranges stay consecutive
-  // (hi of block i is lo of block i + 1), so every page is scored; where the
-  // rounding makes neighbours overlap, a page is scored twice with the same
-  // result.
   auto cut = [&](int i) -> int64_t {
     if (!a.refresh) return total * i / gridDim.x;
-    const int64_t nr = (int64_t)i * (nunits / gridDim.x) + min(i, nunits % (int)gridDim.x);  // refreshes of blocks < i
+    const int64_t nr = (int64_t)i * (nunits / gridDim.x) + min(i, nunits % (int)gridDim.x);
     const int64_t v = (total + (int64_t)kRefreshPages * nunits) * i / gridDim.x - (int64_t)kRefreshPages * nr;
     return v < 0 ? 0 : v > total ? total : v;
   };
   const int64_t lo = cut(blockIdx.x), hi = max(lo, cut(blockIdx.x + 1));
 
-  // partial tiles -> KV-head scores of pages base + 4*kq + wave (waves 0..3,
-  // lanes col == 0 store)
-  auto finish = [&](const f32x4_t (&s)[NT], int buf, float* srow, int base, int lim) {
-    // scaled on the vector ALU before the LDS store (the store never reads an
-    // accumulator straight out of the matrix core)
+  // q of head 16 * wave + col, channel chunk kq + 4m (zero past G); its
+  // non-positive part pairs with k-step m (min row) and its non-negative part
+  // with k-step m + KS / 2 (max row), split on the fly so that q costs 72
+  // registers instead of 144 and two waves fit on each SIMD
+  uint4 qr[KS / 2];
+  auto load_q = [&](int b, int g) {
+    const int h = 16 * wave + col;
+    const uint16_t* qrow = a.q + ((int64_t)b * a.Hq + (int64_t)g * G + min(h, G - 1)) * D;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4_t u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = s[nt][i] * a.scale;
-      part[buf][wave][nt][lane] = u;
-    }
-    __syncthreads();
-    if (wave < 4) {
-      float v = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float x = part[buf][0][nt][lane][wave];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) x += part[buf][w][nt][lane][wave];
-        const bool real = nt * 16 + col < G;
-        x = real ? x : (SUM ? 0.f : -__builtin_inff());
-        v = nt == 0 ? x : (SUM ? v + x : fmaxf(v, x));
-      }
-      v = SUM ? group_sum<16>(v) : group_max_any<16>(v);
-      const int p = base + 4 * kq + wave;
-      if (col == 0 && p < lim) srow[p] = v;
+    for (int m = 0; m < KS / 2; ++m) {
+      const uint4 v = ld16(qrow + 8 * (kq + 4 * m));
+      qr[m] = h < G ? v : make_uint4(0, 0, 0, 0);
     }
   };
-  // this wave's q-/q+ fragments for unit (b, g): head 16nt + col, k-chunk kq + 4*(KW*wave + ks)
-  uint4 qb[NT][KW];
-  auto load_q = [&](int b, int g) {
-    const uint16_t* qrow_b = a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
+  // the 16 x 16 (head x page) bounds: A = q parts, B = bfrag(ks), four accumulators
+  auto mma = [&](auto bfrag, f32x4_t (&acc)[4]) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int j = 0; j < 4; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KW; ++ks) qb[nt][ks] = qq_chunk(qrow_b, nt * 16 + col, G, D, kq + 4 * (KW * wave + ks));
+    for (int m = 0; m < KS / 2; ++m) {
+      uint4 pos;
+      const uint4 neg = split_neg(qr[m], pos);
+      acc[(2 * m) & 3] = mfma16(neg, bfrag(m), acc[(2 * m) & 3]);
+      acc[(2 * m + 1) & 3] = mfma16(pos, bfrag(m + KS / 2), acc[(2 * m + 1) & 3]);
+    }
+  };
+  // lane (kq, col) holds heads 16w + 4kq + i on page col; returns this wave's
+  // KV-head value of page col in every lane of column col
+  auto head_agg = [&](const f32x4_t (&acc)[4]) -> float {
+    float v = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s = (acc[0][i] + acc[1][i]) + (acc[2][i] + acc[3][i]);
+      const float x = 16 * wave + 4 * kq + i < G ? s * a.scale : (SUM ? 0.f : -__builtin_inff());
+      v = i == 0 ? x : (SUM ? v + x : fmaxf(v, x));
+    }
+    return SUM ? rows_sum(v) : rows_max(v);
+  };
+  auto post = [&](float v) {
+    if (wave == 1 && kq == 0) agg[col] = v;
+  };
+  // after a barrier that follows post: wave 0 stores page base + col (if < lim)
+  auto complete = [&](float v, float* srow, int base, int lim) {
+    if (wave == 0 && kq == 0) {
+      const float o = agg[col];
+      if (base + col < lim) srow[base + col] = SUM ? v + o : fmaxf(v, o);
+    }
   };
 
-  int buf = 0;
   // ---- last pages first: rebuild each summary from its valid keys, store it, score it
   for (int ur = blockIdx.x; a.refresh && ur < nunits; ur += gridDim.x) {
     const int b = (u0 + ur) / Hkv, g = (u0 + ur) % Hkv;
@@ -479,29 +486,23 @@ void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs
     const int valid = n - plast * kPage;
     const int dc = D / 8;
     uint16_t* rec = a.summ + (pid * Hkv + g) * 2 * D;
-    __syncthreads();  // rrec of the previous unit is no longer read
-    for (int ci = threadIdx.x; ci < NCH; ci += NTH) {
+    __syncthreads();  // the previous tile or record is no longer read
+    for (int ci = threadIdx.x; ci < NCH; ci += 128) {
       uint4 mn, mx;
       minmax8(a.k + pid * ps + (int64_t)g * hs + 8 * (ci < dc ? ci : ci - dc), ts, valid, mn, mx);
       const uint4 v = ci < dc ? mn : mx;
       *reinterpret_cast<uint4*>(rec + 8 * ci) = v;
-      rrec[ci] = v;
+      tile[ci] = v;
     }
     __syncthreads();
     if (a.topk < P) {
       load_q(b, g);
-      f32x4_t sc[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        sc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KW; ++ks) {
-          const uint4 d = col == 0 ? rrec[kq + 4 * (KW * wave + ks)] : make_uint4(0, 0, 0, 0);
-          sc[nt] = mfma16(d, qb[nt][ks], sc[nt]);
-        }
-      }
-      finish(sc, buf, a.scores + ((int64_t)b * Hkv + g) * a.MP, plast, plast + 1);  // page slot 0 is the last page
-      buf ^= 1;
+      f32x4_t acc[4];
+      mma([&](int ks) { return col == 0 ? tile[kq + 4 * ks] : make_uint4(0, 0, 0, 0); }, acc);
+      const float v = head_agg(acc);
+      post(v);
+      __syncthreads();
+      complete(v, a.scores + ((int64_t)b * Hkv + g) * a.MP, plast, plast + 1);  // page column 0 is the last page
     }
   }
 
@@ -512,73 +513,66 @@ void quest_score_wide_kernel(ScoreArgs a, int G, int Hkv, int64_t ps, int64_t hs
     const int64_t s0 = max(lo, pre[u]) - pre[u], s1 = min(hi, pre[u + 1]) - pre[u];
     if (s1 <= s0) continue;
     const int b = (u0 + u) / Hkv, g = (u0 + u) % Hkv;
-    load_q(b, g);
-    const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
-    float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP;
+    const int npg = (int)(s1 - s0);
+    const int32_t* pt = a.page_table + (int64_t)b * a.MP + s0;
+    float* srow = a.scores + ((int64_t)b * Hkv + g) * a.MP + s0;
     const uint16_t* summ_g = a.summ + (int64_t)g * 2 * D;
-    for (int c0 = (int)s0; c0 < (int)s1; c0 += kWideChunk) {
-      const int npg = min(kWideChunk, (int)s1 - c0);
-      __syncthreads();  // the previous chunk's ids are no longer read
-      stage_i32<(kWideChunk + NTH - 1) / NTH>(ptrow + c0, npg, ids);
+    // page ids in registers: lane l holds page 64 * cw + l (idc) and 64 * (cw + 1) + l (idn), clamped
+    int cw = 0;
+    int idc = pt[min(lane, npg - 1)], idn = pt[min(64 + lane, npg - 1)];
+    load_q(b, g);
+    uint4 r[CPL];
+    // records 16t + 8 * step + 4 * wave + j (j < 4), clamped to the last page
+    // (a repeat that is never stored); all four lie in one 64-page window
+    auto issue = [&](int t, int step) {
+      const int pb = 16 * t + 8 * step + 4 * wave;
+      const int src = (pb >> 6) == cw ? idc : idn;
+      int idj[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) idj[j] = __builtin_amdgcn_readlane(src, min(pb + j, npg - 1) & 63);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int i = 64 * c + lane, j = i / NCH, ch = i % NCH;
+        const int id = j == 0 ? idj[0] : j == 1 ? idj[1] : j == 2 ? idj[2] : idj[3];
+        r[c] = ldnt16(summ_g + (int64_t)id * pid_stride + 8 * ch);
+      }
+    };
+    auto stage = [&](int step) {
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int i = 64 * c + lane, j = i / NCH, ch = i % NCH;
+        const int pg = 8 * step + 4 * wave + j;
+        tile[pg * NCH + (ch ^ (pg & 7))] = r[c];
+      }
+    };
+    // B fragment of k-step ks: chunk kq + 4ks of page col at slot (kq + 4ks) ^ (col & 7)
+    // = 8 * (ks >> 1) + ((kq + 4 * (ks & 1)) ^ (col & 7)): two lane bases, immediate offsets
+    const uint4* tb[2] = {tile + col * NCH + (kq ^ (col & 7)), tile + col * NCH + ((kq + 4) ^ (col & 7))};
+    const int ntile = (npg + 15) / 16;
+    float vprev = 0.f;
+    issue(0, 0);
+    for (int t = 0; t < ntile; ++t) {
+      if ((t >> 2) > cw) {
+        ++cw;
+        idc = idn;
+        idn = pt[min(64 * (cw + 1) + lane, npg - 1)];
+      }
+      __syncthreads();  // tile t - 1 is read by both waves, and wave 1's value of it is posted
+      if (t > 0) complete(vprev, srow, 16 * (t - 1), npg);
+      stage(0);
+      __builtin_amdgcn_sched_barrier(0);  // step 1 lands in the registers step 0 just left
+      issue(t, 1);
+      stage(1);
       __syncthreads();
-      const int ntile = (npg + 15) / 16;
-      auto load = [&](int t, uint4 (&r)[CPT]) {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          const int uu = c * NTH + threadIdx.x;
-          const int p = min(16 * t + uu / NCH, npg - 1);
-          r[c] = ldnt16(summ_g + (int64_t)ids[p] * pid_stride + 8 * (uu % NCH));
-        }
-      };
-      // one LDS tile: the previous tile's fragment reads all precede the
-      // barrier inside its finish, so the next tile may overwrite it
-      auto stage = [&](const uint4 (&r)[CPT]) {
-#pragma unroll
-        for (int c = 0; c < CPT; ++c) {
-          const int uu = c * NTH + threadIdx.x;
-          const int pg = uu / NCH, ch = uu % NCH;
-          tile[pg * NCH + (ch ^ (pg & 7))] = r[c];
-        }
-      };
-      auto score = [&](int t) {
-        f32x4_t sc[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) sc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KW; ++ks) {
-          const int ch = kq + 4 * (KW * wave + ks);
-          const uint4 av = tile[col * NCH + (ch ^ (col & 7))];
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) sc[nt] = mfma16(av, qb[nt][ks], sc[nt]);
-        }
-        finish(sc, buf, srow, c0 + 16 * t, c0 + npg);
-        buf ^= 1;
-      };
-      // RD tiles in the register ring: RD - 1 in flight while one is staged and scored
-      uint4 r[RD][CPT];
-#pragma unroll
-      for (int j = 0; j < RD - 1; ++j) {
-        load(min(j, ntile - 1), r[j]);
-        __builtin_amdgcn_sched_barrier(0);  // issue order = use order
-      }
-      // The prefetch is issued on every step, also past the last tile (a
-      // clamped repeat of it, served by the caches): with a fixed number of
-      // loads between a tile's issue and its use, the compiler waits for that
-      // tile alone instead of draining the whole ring.
-      for (int t = 0; t < ntile; t += RD) {
-#pragma unroll
-        for (int j = 0; j < RD; ++j) {
-          const bool live = j == 0 || t + j < ntile;
-          if (live) stage(r[j]);
-          __syncthreads();
-          load(min(t + j + RD - 1, ntile - 1), r[(j + RD - 1) % RD]);
-          __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of the compute
-          if (live) score(t + j);
-        }
-      }
+      if (t + 1 < ntile) issue(t + 1, 0);
+      f32x4_t acc[4];
+      mma([&](int ks) { return tb[ks & 1][8 * (ks >> 1)]; }, acc);
+      vprev = head_agg(acc);
+      post(vprev);
     }
+    __syncthreads();
+    complete(vprev, srow, 16 * (ntile - 1), npg);
   }
-
 }
 
 static int pick_ppw(int B, int Hkv, int MP) {
@@ -611,16 +605,18 @@ static hipError_t launch_mfma(const Layout& L, const ScoreArgs& a, int G, hipStr
   return hipGetLastError();
 }
 
-template <int D, int NT>
+template <int D>
 static hipError_t launch_wide(const Layout& L, const ScoreArgs& a, int G, hipStream_t st) {
-  // one block of four waves per CU, a three-tile ring (measured on the MLA
-  // workload: 46 us, against 48 us for twelve or six waves and 52-54 us for
-  // deeper rings); units in launches of at most kWideMaxUnits
+  // units in launches of at most kWideUnits
   const int units = a.B * L.hkv;
-  for (int u0 = 0; u0 < units; u0 += kWideMaxUnits) {
-    const int nu = units - u0 < kWideMaxUnits ? units - u0 : kWideMaxUnits;
-    hipLaunchKernelGGL((quest_score_wide_kernel<D, NT, 3, kWideWaves>), dim3(256), dim3(kWideWaves * 64), 0, st, a, G,
-                       L.hkv, L.ps, L.hs, L.ts, u0, nu);
+  for (int u0 = 0; u0 < units; u0 += kWideUnits) {
+    const int nu = units - u0 < kWideUnits ? units - u0 : kWideUnits;
+    if (a.head_sum)
+      hipLaunchKernelGGL((quest_score_wide_kernel<D, true>), dim3(256 * kWideBlocksPerCU), dim3(128), 0, st, a, G, L.hkv,
+                         L.ps, L.hs, L.ts, u0, nu);
+    else
+      hipLaunchKernelGGL((quest_score_wide_kernel<D, false>), dim3(256 * kWideBlocksPerCU), dim3(128), 0, st, a, G,
+                         L.hkv, L.ps, L.hs, L.ts, u0, nu);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -632,7 +628,7 @@ hipError_t launch_quest_scores(const Layout& L, const ScoreArgs& a, hipStream_t 
   if (a.B == 0 || a.MP == 0) return hipSuccess;
   if (L.dk == 64) return G <= 16 ? launch_mfma<64, 1>(L, a, G, st) : launch_mfma<64, 2>(L, a, G, st);
   if (L.dk == 128) return G <= 16 ? launch_mfma<128, 1>(L, a, G, st) : launch_mfma<128, 2>(L, a, G, st);
-  if (L.dk == 576) return G <= 16 ? launch_wide<576, 1>(L, a, G, st) : launch_wide<576, 2>(L, a, G, st);
+  if (L.dk == 576) return launch_wide<576>(L, a, G, st);
   return hipErrorInvalidValue;
 }
 

@@ -347,20 +347,37 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a, int 
   __shared__ int vld_lds[PPS];
 
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int nsplit = gridDim.x;
+  const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int col = lane & 15, kq = lane >> 4;
+  // The request's length, q and the split's page ids are requested together,
+  // before any of them is used: the ids are read up to the split's nominal
+  // size within their row (entries past the request's pages are staged but
+  // never used), so the first page loads wait for one memory round trip
+  // instead of three dependent ones.
   const int n = a.seq_lens[b];
-  const int P = (n + kPage - 1) / kPage;
+  uint4 qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qf[ks] = ld16(a.q + (head0 + min(col, G - 1)) * D + 8 * kq + 32 * ks);  // unconditional: loads issue together
   const int32_t* list = nullptr;
   const int32_t* plist = nullptr;
-  int kk = P;
   if (a.selected) {
-    kk = min(a.topk, P);
     list = a.selected + ((int64_t)b * Hkv + g) * a.topk;
     if (a.selected_phys) plist = a.selected_phys + ((int64_t)b * Hkv + g) * a.topk;
   }
   const int p_begin = split * pps;
+  const int rowlen = a.selected ? a.topk : a.MP;
+  for (int i = threadIdx.x; i < pps; i += blockDim.x) {
+    const int idx = min(p_begin + i, rowlen - 1);
+    const int lp = list ? list[idx] : idx;
+    pid_lds[i] = plist ? plist[idx] : a.page_table[(int64_t)b * a.MP + min(max(lp, 0), a.MP - 1)];
+    vld_lds[i] = lp;  // turned into a token count below, by the same thread
+  }
+  const int P = (n + kPage - 1) / kPage;
+  const int kk = a.selected ? min(a.topk, P) : P;
   const int npg = max(0, min(p_begin + pps, kk) - p_begin);
-  const int nsplit = gridDim.x;
-  const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * G;
   if (npg == 0) {
     if (FINAL) {  // an empty request: a zero output row
       for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) a.out[head0 * D + idx] = 0.f;
@@ -372,21 +389,10 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a, int 
     }
     return;
   }
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int col = lane & 15, kq = lane >> 4;
-  // q fragments first: independent of the page ids, so both loads overlap
-  uint4 qf[4];
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
-    qf[ks] = ld16(a.q + (head0 + min(col, G - 1)) * D + 8 * kq + 32 * ks);  // unconditional: loads issue together
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     if (col >= G) qf[ks] = make_uint4(0, 0, 0, 0);
-  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
-    const int lp = list ? list[p_begin + i] : p_begin + i;
-    pid_lds[i] = plist ? plist[p_begin + i] : a.page_table[(int64_t)b * a.MP + lp];
-    vld_lds[i] = min(kPage, n - lp * kPage);
-  }
+  for (int i = threadIdx.x; i < npg; i += blockDim.x) vld_lds[i] = min(kPage, n - vld_lds[i] * kPage);
   __syncthreads();
 
   const int npw = npg > w ? (npg - w + NW - 1) / NW : 0;  // pages of this wave: w + NW*ii
@@ -617,34 +623,14 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
   const int split = blockIdx.x % nsplit, hblk = blockIdx.x / nsplit, g = blockIdx.y, b = blockIdx.z;
   const int Gall = a.Hq / Hkv;
   const int G = min(16 * NHT, Gall - 16 * NHT * hblk);  // query heads of this block
-  const int n = a.seq_lens[b];
-  const int P = (n + kPage - 1) / kPage;
-  const int32_t* list = nullptr;
-  const int32_t* plist = nullptr;
-  int kk = P;
-  if (a.selected) {
-    kk = min(a.topk, P);
-    list = a.selected + ((int64_t)b * Hkv + g) * a.topk;
-    if (a.selected_phys) plist = a.selected_phys + ((int64_t)b * Hkv + g) * a.topk;
-  }
-  const int p_begin = split * pps;
-  const int npg = max(0, min(p_begin + pps, kk) - p_begin);
   const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * Gall + 16 * NHT * hblk;
-  if (npg == 0) {
-    for (int h = threadIdx.x; h < G; h += blockDim.x) {
-      a.part_ml[((head0 + h) * nsplit + split) * 2] = -__builtin_inff();
-      a.part_ml[((head0 + h) * nsplit + split) * 2 + 1] = 0.f;
-    }
-    return;
-  }
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int col = lane & 15, kq = lane >> 4;
-  const uint16_t* kb = a.k + (int64_t)g * hs;
-  const uint16_t* vrow = kb + 128 * w + 8 * col + (4 * kq) * ts;  // + e * ts: value rows 4kq + e
-  const uint16_t* rrow = kb + col * ts + 512 + 16 * w + 4 * kq;   // rope: token col, 4 channels
-
+  // The request's length, q and the split's page ids are requested together,
+  // before any of them is used (the ids up to the split's nominal size within
+  // their row; entries past the request's pages are staged but never used).
+  const int n = a.seq_lens[b];
   // q fragments: head 16ht + col; latent channels 128w + 32ks + 8kq, rope 512 + 16w + 4kq
-  // (requested first: their latency overlaps the page-id staging below)
   uint4 qf[NHT][4];
   uint2 qr[NHT];
 #pragma unroll
@@ -655,11 +641,34 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
     for (int ks = 0; ks < 4; ++ks) qf[ht][ks] = ld16(qh + 128 * w + 32 * ks + 8 * kq);
     qr[ht] = *reinterpret_cast<const uint2*>(qh + 512 + 16 * w + 4 * kq);
   }
-  for (int i = threadIdx.x; i < npg; i += blockDim.x) {
-    const int lp = list ? list[p_begin + i] : p_begin + i;
-    pid_lds[i] = plist ? plist[p_begin + i] : a.page_table[(int64_t)b * a.MP + lp];
-    vld_lds[i] = min(kPage, n - lp * kPage);
+  const int32_t* list = nullptr;
+  const int32_t* plist = nullptr;
+  if (a.selected) {
+    list = a.selected + ((int64_t)b * Hkv + g) * a.topk;
+    if (a.selected_phys) plist = a.selected_phys + ((int64_t)b * Hkv + g) * a.topk;
   }
+  const int p_begin = split * pps;
+  const int rowlen = a.selected ? a.topk : a.MP;
+  for (int i = threadIdx.x; i < pps; i += blockDim.x) {
+    const int idx = min(p_begin + i, rowlen - 1);
+    const int lp = list ? list[idx] : idx;
+    pid_lds[i] = plist ? plist[idx] : a.page_table[(int64_t)b * a.MP + min(max(lp, 0), a.MP - 1)];
+    vld_lds[i] = lp;  // turned into a token count below, by the same thread
+  }
+  const int P = (n + kPage - 1) / kPage;
+  const int kk = a.selected ? min(a.topk, P) : P;
+  const int npg = max(0, min(p_begin + pps, kk) - p_begin);
+  if (npg == 0) {
+    for (int h = threadIdx.x; h < G; h += blockDim.x) {
+      a.part_ml[((head0 + h) * nsplit + split) * 2] = -__builtin_inff();
+      a.part_ml[((head0 + h) * nsplit + split) * 2 + 1] = 0.f;
+    }
+    return;
+  }
+  for (int i = threadIdx.x; i < npg; i += blockDim.x) vld_lds[i] = min(kPage, n - vld_lds[i] * kPage);
+  const uint16_t* kb = a.k + (int64_t)g * hs;
+  const uint16_t* vrow = kb + 128 * w + 8 * col + (4 * kq) * ts;  // + e * ts: value rows 4kq + e
+  const uint16_t* rrow = kb + col * ts + 512 + 16 * w + 4 * kq;   // rope: token col, 4 channels
   __syncthreads();
 #pragma unroll
   for (int ht = 0; ht < NHT; ++ht) {

@@ -94,51 +94,65 @@ __device__ __forceinline__ void block_and_or(uint32_t& vand, uint32_t& vor, Topk
   }
 }
 
-// Requires 0 < k < N <= KPT * 1024.  Writes k indices (plus idx_base) into
-// out[0..k) and, when `translate` is given, translate[index] into out2[0..k).
-// Indices below `forced_lo` or from `forced_hi` on take the largest key, so
-// they are always kept (their number must not exceed k).
+// A thread's KPT consecutive scores and their translations, as loaded.
 template <int KPT>
-__device__ __forceinline__ void block_topk(const float* __restrict__ row, int N, int k, int32_t* __restrict__ out,
-                                           TopkShared& sm,
-                           const int32_t* __restrict__ translate = nullptr, int32_t* __restrict__ out2 = nullptr,
-                           int forced_lo = 0, int forced_hi = 0x7fffffff, int idx_base = 0) {
-  const int tid = threadIdx.x;
-  const int base = tid * KPT;
-  uint32_t key[KPT];
-  int32_t tr[KPT];
-  uint32_t kand = 0xffffffffu, kor = 0u;
-  const bool full = base + KPT <= N;
+struct TopkRow {
+  float f[KPT];
+  int32_t t[KPT];
+};
+
+// Loads entries tid*KPT .. tid*KPT + KPT-1 of a row holding `avail` entries
+// (16 bytes per load where the run is whole and aligned; zeros past the row).
+// Needs no selection parameters, so a caller can request it before it knows
+// how many of the entries will take part.
+template <int KPT>
+__device__ __forceinline__ void topk_load(const float* __restrict__ row, int avail,
+                                          const int32_t* __restrict__ translate, TopkRow<KPT>& r) {
+  const int base = threadIdx.x * KPT;
+  const bool full = base + KPT <= avail;
   if (KPT >= 4 && full && (((uintptr_t)row) & 15) == 0) {
 #pragma unroll
     for (int i = 0; i < KPT; i += 4) {
       const float4 f = *reinterpret_cast<const float4*>(row + base + i);
-      key[i] = float_key(f.x);
-      key[i + 1] = float_key(f.y);
-      key[i + 2] = float_key(f.z);
-      key[i + 3] = float_key(f.w);
+      r.f[i] = f.x;
+      r.f[i + 1] = f.y;
+      r.f[i + 2] = f.z;
+      r.f[i + 3] = f.w;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) key[i] = (base + i < N) ? float_key(row[base + i]) : 0u;
+    for (int i = 0; i < KPT; ++i) r.f[i] = (base + i < avail) ? row[base + i] : 0.f;
   }
-  // the translations are fetched with the keys, off the critical path (16
-  // bytes per load where the run is whole and aligned)
   if (translate) {
     if (KPT >= 4 && full && (((uintptr_t)translate) & 15) == 0) {
 #pragma unroll
       for (int i = 0; i < KPT; i += 4) {
         const int4 t4 = *reinterpret_cast<const int4*>(translate + base + i);
-        tr[i] = t4.x;
-        tr[i + 1] = t4.y;
-        tr[i + 2] = t4.z;
-        tr[i + 3] = t4.w;
+        r.t[i] = t4.x;
+        r.t[i + 1] = t4.y;
+        r.t[i + 2] = t4.z;
+        r.t[i + 3] = t4.w;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) tr[i] = (base + i < N) ? translate[base + i] : 0;
+      for (int i = 0; i < KPT; ++i) r.t[i] = (base + i < avail) ? translate[base + i] : 0;
     }
   }
+}
+
+// Selection over loaded entries (see block_topk); entries at N and past are
+// ignored.  out2 is written only when translations were loaded.
+template <int KPT>
+__device__ __forceinline__ void block_topk_loaded(const TopkRow<KPT>& r, int N, int k, int32_t* __restrict__ out,
+                                                  TopkShared& sm, int32_t* __restrict__ out2, int forced_lo,
+                                                  int forced_hi, int idx_base) {
+  const int tid = threadIdx.x;
+  const int base = tid * KPT;
+  uint32_t key[KPT];
+  const int32_t* tr = r.t;
+  uint32_t kand = 0xffffffffu, kor = 0u;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) key[i] = (base + i < N) ? float_key(r.f[i]) : 0u;
 #pragma unroll
   for (int i = 0; i < KPT; ++i)
     if (base + i < forced_lo || base + i >= forced_hi) key[i] = 0xffffffffu;
@@ -253,6 +267,20 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ row, int N,
   }
 }
 
+// Requires 0 < k < N <= KPT * 1024.  Writes k indices (plus idx_base) into
+// out[0..k) and, when `translate` is given, translate[index] into out2[0..k).
+// Indices below `forced_lo` or from `forced_hi` on take the largest key, so
+// they are always kept (their number must not exceed k).
+template <int KPT>
+__device__ __forceinline__ void block_topk(const float* __restrict__ row, int N, int k, int32_t* __restrict__ out,
+                                           TopkShared& sm, const int32_t* __restrict__ translate = nullptr,
+                                           int32_t* __restrict__ out2 = nullptr, int forced_lo = 0,
+                                           int forced_hi = 0x7fffffff, int idx_base = 0) {
+  TopkRow<KPT> r;
+  topk_load<KPT>(row, N, translate, r);
+  block_topk_loaded<KPT>(r, N, k, out, sm, translate ? out2 : nullptr, forced_lo, forced_hi, idx_base);
+}
+
 // ---------------------------------------------------------------------------
 // Quest: pages of (b, g).  P = ceil(seq_len/16).  Forced pages: [0, s) and
 // [r_lo, P) with s = min(sink, P), r_lo = max(P - recent, s); the row holds
@@ -267,13 +295,17 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(const float* _
                                                                   int topk, int sink, int recent) {
   __shared__ TopkShared sm;
   const int b = blockIdx.y, g = blockIdx.x;
+  const int32_t* ptrow = page_table ? page_table + (int64_t)b * MP : nullptr;
+  // the request's length and the whole score row (with its page ids) are
+  // requested together: the row's loads do not wait for the length
   const int n = seq_lens[b];
+  TopkRow<KPT> row;
+  if (topk > 0) topk_load<KPT>(scores + ((int64_t)b * Hkv + g) * MP, MP, ptrow, row);
   const int P = (n + kPage - 1) / kPage;
   const int cap = topk + sink + recent;
   const int kk = min(cap, P);
   int32_t* out = selected + ((int64_t)b * Hkv + g) * cap;
   int32_t* out2 = phys ? phys + ((int64_t)b * Hkv + g) * cap : nullptr;
-  const int32_t* ptrow = page_table ? page_table + (int64_t)b * MP : nullptr;
   for (int i = kk + threadIdx.x; i < cap; i += blockDim.x) {
     out[i] = -1;
     if (out2) out2[i] = -1;
@@ -295,7 +327,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_pages_kernel(const float* _
     }
     return;
   }
-  block_topk<KPT>(scores + ((int64_t)b * Hkv + g) * MP, P, kk, out, sm, ptrow, out2, s_end, r_lo);
+  block_topk_loaded<KPT>(row, P, kk, out, sm, ptrow ? out2 : nullptr, s_end, r_lo, 0);
 }
 
 static int pick_kpt(int n) {

@@ -372,10 +372,11 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
 // per-tile chain of barriers and cross-wave sums, not by the memory.
 // ---------------------------------------------------------------------------
 // A last-page rebuild and score counted as this many pages of a block's share
-// (measured with the block-cooperative form: 46.4 us with the rebuilds after
-// the shares, 45.8 / 45.4 / 44.9 us with them first at 16 / 32 / 48 pages,
-// and 44.9 us with no rebuild at all)
-constexpr int kRefreshPages = 48;
+// (its chain of dependent loads takes about as long as 80 pages of streaming
+// under full load; MLA ragged batch: 42.4 / 41.9 / 41.1 / 42.1 us at 48 / 64
+// / 80 / 96 pages, events; rebuilding after the shares instead measured
+// slower in an earlier form of this kernel)
+constexpr int kRefreshPages = 80;
 constexpr int kWideUnits = 256;       // units per launch (prefix sums live in LDS)
 constexpr int kWideBlocksPerCU = 2;   // one wave per SIMD: more waves in flight made this record stream slower
 
@@ -479,6 +480,7 @@ __global__ __launch_bounds__(128) void quest_score_wide_kernel(ScoreArgs a, int 
   for (int ur = blockIdx.x; a.refresh && ur < nunits; ur += gridDim.x) {
     const int b = (u0 + ur) / Hkv, g = (u0 + ur) % Hkv;
     const int n = a.seq_lens[b];
+    load_q(b, g);  // with the page lookup: the rebuild's chain of dependent loads is long enough
     const int P = (n + kPage - 1) / kPage;
     if (P == 0) continue;
     const int plast = P - 1;
@@ -496,7 +498,6 @@ __global__ __launch_bounds__(128) void quest_score_wide_kernel(ScoreArgs a, int 
     }
     __syncthreads();
     if (a.topk < P) {
-      load_q(b, g);
       f32x4_t acc[4];
       mma([&](int ks) { return col == 0 ? tile[kq + 4 * ks] : make_uint4(0, 0, 0, 0); }, acc);
       const float v = head_agg(acc);

@@ -202,18 +202,27 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
 
   const int b = blockIdx.z, g = blockIdx.y;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int n = a.seq_lens[b];
-  const int P = (n + kPage - 1) / kPage;
-  const bool dense = a.topk >= P;
   const int blk_start = blockIdx.x * 4 * ppw;
-  if (blk_start >= P) return;
-  const int blk_end = min(blk_start + 4 * ppw, P);
-  const int plast = P - 1;
   const int32_t* ptrow = a.page_table + (int64_t)b * a.MP;
   const uint16_t* qrow_b = a.q + ((int64_t)b * a.Hq + (int64_t)g * G) * D;
   const int col = lane & 15, kq = lane >> 4;  // A: page slot / B: head; k-chunk quarter
 
-  if (!dense) stage_i32<4 * kMaxPagesPerWave / 256>(ptrow + blk_start, blk_end - blk_start, ids);
+  // The request's length, q and the block's page ids are requested together
+  // (the ids over the block's nominal range within the row: entries past the
+  // request's pages are staged but never read), so the first records wait for
+  // one memory round trip instead of two dependent ones.
+  const int n = a.seq_lens[b];
+  uint4 qb[NT][KS];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qb[nt][ks] = qq_chunk(qrow_b, nt * 16 + col, G, D, kq + 4 * ks);
+  auto bfrag = [&](int nt, int ks) -> uint4 { return qb[nt][ks]; };
+  stage_i32<4 * kMaxPagesPerWave / 256>(ptrow + blk_start, min(4 * ppw, a.MP - blk_start), ids);
+  const int P = (n + kPage - 1) / kPage;
+  const bool dense = a.topk >= P;
+  if (blk_start >= P) return;
+  const int plast = P - 1;
   __syncthreads();
 
   const int start = blk_start + wave * ppw;
@@ -222,13 +231,6 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(ScoreArgs a, int 
   const bool do_refresh = a.refresh && plast >= start && plast < end;
   if (dense && !do_refresh) return;
   if (a.refresh) end = min(end, plast);
-
-  uint4 qb[NT][KS];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[nt][ks] = qq_chunk(qrow_b, nt * 16 + col, G, D, kq + 4 * ks);
-  auto bfrag = [&](int nt, int ks) -> uint4 { return qb[nt][ks]; };
 
   const uint16_t* summ_g0 = a.summ + (int64_t)g * 2 * D;
   const int64_t pid_stride = (int64_t)Hkv * 2 * D;

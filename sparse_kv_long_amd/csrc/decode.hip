@@ -7,17 +7,15 @@
 // the valid tokens (t < seq_len) of the pages kept for (request, g) -- all of
 // the request's pages in dense mode.
 //
-// One block per (split, KV head, request).  A split owns up to PPS kept pages.
-//   phase A  q.k: LPT lanes share a token row (16-byte loads of LPT adjacent
-//            chunks per instruction), q of the wave's HW heads sits in
-//            registers, v_dot2 partial sums are combined over the LPT lanes
-//            with DPP.  Logits (log2 domain) go to LDS, token-major.
-//   phase B  per head: max and sum of 2^(z - max) over the split's tokens.
-//   phase C  p.v: each lane owns 8 value channels of one token row, heads'
-//            weights are read from LDS, fp32 FMA accumulation; the token
-//            groups are then folded together with cross-lane shuffles.
-// The split writes (max, sum, unnormalised acc); the merge kernel combines the
-// splits of each head: out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
+// Three kernels compute it, one block per (split, KV head, request), a split
+// owning up to PPS kept pages: the matrix-core kernel for head dimension 128
+// with up to 16 query heads per KV head (decode_mfma_kernel), the one for the
+// 576/512 latent layout (decode_mla_kernel), and a vector-ALU kernel for the
+// other shapes, or for every shape when the caller asks for it
+// (decode_kernel).  Each split writes (max, sum, unnormalised acc) -- or,
+// when it is the request's only split, the matrix-core GQA kernel writes the
+// output itself -- and the merge kernel combines the splits of each head:
+// out = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s.
 #include "common.h"
 #include "se_internal.h"
 
@@ -52,9 +50,17 @@ struct DecodeShape {
   static_assert(DK % (LPT * 8) == 0 && DV % 8 == 0 && LPV <= kWave, "unsupported head dims");
 };
 
-// Each wave runs q.k -> softmax -> p.v on its own pages with wave-private
-// LDS; the only block barriers are after the page-id staging and before the
-// final merge of the waves that share a head group.
+// Vector-ALU decode.  Each wave runs q.k -> softmax -> p.v on its own pages
+// with wave-private LDS; the only block barriers are after the page-id
+// staging and before the final merge of the waves that share a head group.
+//   phase A  q.k: LPT lanes share a token row (16-byte loads of LPT adjacent
+//            chunks per instruction), q of the wave's HW heads sits in
+//            registers, v_dot2 partial sums are combined over the LPT lanes
+//            with DPP.  Logits (log2 domain) go to LDS, token-major.
+//   phase B  per head: max and sum of 2^(z - max) over the wave's tokens.
+//   phase C  p.v: each lane owns 8 value channels of one token row, heads'
+//            weights are read from LDS, fp32 FMA accumulation; the token
+//            groups are then folded together with cross-lane shuffles.
 template <int G, int DK, int DV, bool VISK>
 __global__ __launch_bounds__((DecodeShape<G, DK, DV>::NW * 64))
 __attribute__((amdgpu_waves_per_eu(DK > 128 ? 2 : G == 16 ? 3 : 4))) void decode_kernel(DecodeArgs a, int Hkv,

@@ -8,16 +8,10 @@
 // Page score: each query head h bounds every logit of page p by
 //   U = s * sum_c max(q_c * min_c, q_c * max_c) = s * (q+ . max + q- . min)
 // with q+ = max(q, 0) and q- = min(q, 0) (exact: one term of each channel is
-// 0 * finite).  Both halves are bf16 dot products, so the score is 2D packed
-// v_dot2 operations per head.  The KV head's score is the max (or sum) of
-// its query heads' bounds.
-//
-// Work layout of the fast kernel: 8 lanes read one 2*D-element record with
-// 16-byte loads (a record of D = 128 is 512 B: lanes 0-7 read chunks 0-7,
-// then 8-15, ...), so one wave instruction covers 8 records; each lane owns
-// the same channel chunks of the min half and the max half, keeps q+ and q-
-// of those channels for all G heads in registers, and the 8 partial sums of
-// a record are combined with three DPP steps.
+// 0 * finite).  Both halves are bf16 contractions over the 2D-element
+// summary record, so the bounds of 16 pages x 16 heads are one matrix-core
+// tile per 32 k-elements (K1 below).  The KV head's score is the max (or sum)
+// of its query heads' bounds.
 #include <stdlib.h>
 #include <string.h>
 
@@ -158,15 +152,17 @@ __device__ __forceinline__ void minmax8(const uint16_t* src, int64_t ts, int val
 }
 
 // ---------------------------------------------------------------------------
-// K1, matrix-core kernel.  The page bound is a dense contraction,
+// K1, matrix-core kernel (Dk 64 and 128).  The page bound is a dense
+// contraction,
 //   score[page][h] = sum_k rec[page][k] * qq[h][k],  k < 2D,
 // with rec = [min | max] (the stored summary record) and qq = [q- | q+], so
 // it runs on v_mfma_f32_16x16x32_bf16: 16 pages x 16 heads x 32 k per
-// instruction, fp32 accumulation of exact bf16 products.  Lane l supplies
-// page l%16 and k-chunk l/16 (+4 per k step) of the record, i.e. 16-byte
-// loads that form 64-byte contiguous runs; the output element i of lane l is
-// page 4*(l/16)+i, head l%16, so the KV-head max (or sum) is a 16-lane DPP
-// reduction.  qq fragments sit in registers.
+// instruction, fp32 accumulation of exact bf16 products.  Each wave fetches
+// its records 8 lanes per record (whole 128-byte lines), stages them in its
+// LDS tile and reads them back in the A layout (lane l: page l%16, k-chunk
+// l/16 + 4 per k step); the output element i of lane l is page 4*(l/16)+i,
+// head l%16, so the KV-head max (or sum) is a 16-lane DPP reduction.  qq
+// fragments sit in registers.
 // The wave that owns a request's last page rebuilds that page's summary from
 // its keys with all 64 lanes (each lane one 16-byte chunk: min or max of 8
 // channels over the valid tokens), stores it, and scores it from LDS.

@@ -613,10 +613,17 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a, int 
 constexpr int kMlaPagesPerSplit = 512;
 constexpr int kMlaTargetBlocks = 512;  // two resident blocks per CU
 constexpr int kMlaHeadsPerBlock = 16;
+// With an even split count the splits form two halves, the first dispatched
+// first: its blocks are the older of the two on each CU and win its issue
+// arbitration (clock stamps: their page loops took 15.7 us against 19.4 us),
+// so the first half's splits hold about 15% more pages (MLA ragged batch:
+// 18 and 14 of 256; decode + merge 35.1 against 35.9 us, 35.3 at 30%)
+constexpr int kMlaSplitTilt = 150;  // first-half splits longer by this / 1024
 
 template <int NHT, int RD, int WPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
-void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts, int pps, float scale2, int nhb) {
+void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts, int pps, int pps1, float scale2,
+                       int nhb) {
   constexpr int DK = 576, DV = 512, NW = 4, PPS = kMlaPagesPerSplit;
   __shared__ uint4 stage[NW][2][kPage * 16];      // per wave and page of the pair: 16 tokens x 16 chunks, swizzled
   __shared__ f32x4_t sbuf[2][NW][2 * NHT][kWave];  // partial logits (head tile, page), double-buffered over pairs
@@ -624,9 +631,13 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
   __shared__ int64_t pid_lds[PPS];
   __shared__ int vld_lds[PPS];
 
-  // grid x: splits x head blocks (16 * NHT query heads each)
-  const int nsplit = gridDim.x / nhb;
-  const int split = blockIdx.x % nsplit, hblk = blockIdx.x / nsplit, g = blockIdx.y, b = blockIdx.z;
+  // grid x: splits of one half x head blocks (16 * NHT query heads each);
+  // z: halves x requests.  The first half's splits (dispatched first) hold
+  // pps pages each, the second half's pps1.
+  const int halves = gridDim.z / a.B, nsh = gridDim.x / nhb, nsplit = nsh * halves;
+  const int half = blockIdx.z / a.B, b = blockIdx.z % a.B, g = blockIdx.y;
+  const int split = half * nsh + blockIdx.x % nsh, hblk = blockIdx.x / nsh;
+  const int my_pps = half == 0 ? pps : pps1;
   const int Gall = a.Hq / Hkv;
   const int G = min(16 * NHT, Gall - 16 * NHT * hblk);  // query heads of this block
   const int64_t head0 = (int64_t)b * a.Hq + (int64_t)g * Gall + 16 * NHT * hblk;
@@ -653,9 +664,9 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
     list = a.selected + ((int64_t)b * Hkv + g) * a.topk;
     if (a.selected_phys) plist = a.selected_phys + ((int64_t)b * Hkv + g) * a.topk;
   }
-  const int p_begin = split * pps;
+  const int p_begin = half == 0 ? split * pps : nsh * pps + (split - nsh) * pps1;
   const int rowlen = a.selected ? a.topk : a.MP;
-  for (int i = threadIdx.x; i < pps; i += blockDim.x) {
+  for (int i = threadIdx.x; i < my_pps; i += blockDim.x) {
     const int idx = min(p_begin + i, rowlen - 1);
     const int lp = list ? list[idx] : idx;
     pid_lds[i] = plist ? plist[idx] : a.page_table[(int64_t)b * a.MP + min(max(lp, 0), a.MP - 1)];
@@ -663,7 +674,7 @@ void decode_mla_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts
   }
   const int P = (n + kPage - 1) / kPage;
   const int kk = a.selected ? min(a.topk, P) : P;
-  const int npg = max(0, min(p_begin + pps, kk) - p_begin);
+  const int npg = max(0, min(p_begin + my_pps, kk) - p_begin);
   if (npg == 0) {
     for (int h = threadIdx.x; h < G; h += blockDim.x) {
       a.part_ml[((head0 + h) * nsplit + split) * 2] = -__builtin_inff();
@@ -1125,11 +1136,25 @@ static hipError_t launch_mfma_g(const Layout& L, const DecodeArgs& a, int pps, h
 static hipError_t launch_mla(const Layout& L, const DecodeArgs& a, int pps, hipStream_t st) {
   const float scale2 = a.scale * kLog2e;
   const int nhb = (a.Hq / L.hkv + kMlaHeadsPerBlock - 1) / kMlaHeadsPerBlock;
-  dim3 grid(a.splits * nhb, L.hkv, a.B);
+  // two halves of the splits when their count is even: the first half,
+  // dispatched first and so older on its CUs, takes longer splits
+  const int kmax = a.selected ? (a.topk < a.MP ? a.topk : a.MP) : a.MP;
+  int halves = 1, p0 = pps, p1 = pps;
+  if (kMlaSplitTilt > 0 && a.splits % 2 == 0) {
+    const int nsh = a.splits / 2;
+    p1 = (int)((int64_t)kmax * 1024 / ((int64_t)nsh * (2048 + kMlaSplitTilt)));
+    p0 = (kmax - nsh * p1 + nsh - 1) / nsh;
+    if (p1 >= 1 && p0 <= kMlaPagesPerSplit) {
+      halves = 2;
+    } else {
+      p0 = p1 = pps;
+    }
+  }
+  dim3 grid(a.splits / halves * nhb, L.hkv, a.B * halves);
   // 16 heads per block, a four-page register ring (one pair in flight while
   // one is processed), two waves per SIMD (measured: 35.8 us against 38.7 us
   // for one 32-head block with a six-page ring at one wave per SIMD)
-  hipLaunchKernelGGL((decode_mla_kernel<1, 4, 2>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, pps, scale2,
+  hipLaunchKernelGGL((decode_mla_kernel<1, 4, 2>), grid, dim3(256), 0, st, a, L.hkv, L.ps, L.hs, L.ts, p0, p1, scale2,
                      nhb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

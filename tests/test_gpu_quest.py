@@ -25,6 +25,11 @@ SMALL = {
     "d64_g16": (QuestWorkload("t_d64_g16", 1, 16, 1, 64, 64, 1000, 9, "none", seed=18), [1000]),
     "mla": (QuestWorkload("t_mla", 2, 32, 1, 576, 512, 1000, 16, "none", v_is_k_prefix=True, seed=19), [1000, 455]),
     "mla_g8": (QuestWorkload("t_mla_g8", 1, 8, 1, 576, 512, 600, 5, "none", v_is_k_prefix=True, seed=20), [600]),
+    # a 40-page budget: with an even split count the latent-layout decode's
+    # splits come in two halves of unequal length; the short requests leave
+    # whole splits of either half empty
+    "mla_k40": (QuestWorkload("t_mla_k40", 3, 32, 1, 576, 512, 2000, 40, "none", v_is_k_prefix=True, seed=24),
+                [2000, 600, 17]),
 }
 
 
@@ -136,6 +141,17 @@ def test_sparse_decode_matches_oracle(name):
     wl, x, out, sel, ref = _decode_case(name)
     vmax = float(torch.nan_to_num(x["v_pages"] if x["v_pages"] is not None else x["k_pages"], 0.0).abs().max())
     check_attention(to_np(out), ref, vmax, name)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 4, 8, 16])
+def test_latent_decode_split_halves_match_oracle(splits):
+    """Even split counts put the latent-layout decode's splits in two halves,
+    the first with longer splits (40 pages over 4 splits: 11 + 11 + 9 + 9;
+    over 16: eight of 3 and eight of 2); odd counts keep equal splits.  Selection by the gap rule and attention against the
+    oracle, for requests of 125, 38 and 2 pages."""
+    wl, x, out, sel, ref = _decode_case("mla_k40", splits=splits)
+    vmax = float(torch.nan_to_num(x["k_pages"], 0.0).abs().max())
+    check_attention(to_np(out), ref, vmax, f"mla_k40 splits {splits}")
 
 
 @pytest.mark.parametrize("splits", [0, 1, 3])

@@ -159,24 +159,32 @@ __device__ __forceinline__ void load_k_frags(const uint16_t* kbase, int kt, int 
 
 // ---------------------------------------------------------------------------
 // Pass 1: partial row max / sum of 2^z (log2-domain logits).
-// Grid (nblk, Hkv * nrg, B), 4 waves, wave slot = blockIdx.x*4 + wave; or
-// with RGW grid (nblk, Hkv, B), nrg waves, wave = row group, slot = blockIdx.x.
+// Grid (Hkv * nrg, B, nblk), 4 waves, wave slot = blockIdx.z*4 + wave; or
+// with RGW grid (Hkv, B, nblk), nrg waves, wave = row group, slot = blockIdx.z.
+// The walkers of a unit are the slowest grid dimension, so each unit has
+// blocks in every dispatch round: blocks dispatched in a later round are the
+// younger ones on their CUs and lose the issue arbitration (clock stamps:
+// second-round blocks ended about 7% later), and a unit whose blocks all
+// fell in the last round finished last.  Measured (kernel trace, 32K
+// prompts): row statistics + votes 405.4 against 411.9 us for SnapKV's
+// window, 1111 against 1136 us for H2O's; giving the first round's walkers
+// a larger share of the key tiles measured no better.
 // ---------------------------------------------------------------------------
 template <int D, int NRT, bool RGW>
 __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_rowstats_kernel(SnapArgs a,
                                                                                     float* __restrict__ row_part,
                                                                                     int nrg, int slots, int skip_kept,
                                                                                     float scale2) {
-  const int b = blockIdx.z;
-  const int g = RGW ? blockIdx.y : blockIdx.y / nrg;
-  const int rg = RGW ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : blockIdx.y % nrg;
+  const int b = blockIdx.y;
+  const int g = RGW ? blockIdx.x : blockIdx.x / nrg;
+  const int rg = RGW ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : blockIdx.x % nrg;
   const int n = a.lens[b];
   const int L = n - a.W;
   if (L <= 0 || (skip_kept && nothing_dropped(a, n))) return;
   const int G = a.Hq / a.Hkv;
   const int rows = G * a.W;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = RGW ? (int)blockIdx.x : (int)blockIdx.x * kSnapWaves + wave;
+  const int slot = RGW ? (int)blockIdx.z : (int)blockIdx.z * kSnapWaves + wave;
 
   uint4 qf[NRT][D / 16];
   load_q_frags<D, NRT>(a, b, g, rg, rows, qf);
@@ -292,16 +300,16 @@ __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_votes_kerne
                                                                                  int slots, int skip_kept,
                                                                                  float scale2) {
   __shared__ float c_lds[RGW ? kMaxRgWaves : 1][kRowsPerGroup];
-  const int b = blockIdx.z;
-  const int g = RGW ? blockIdx.y : blockIdx.y / nrg;
-  const int rg = RGW ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : blockIdx.y % nrg;
+  const int b = blockIdx.y;
+  const int g = RGW ? blockIdx.x : blockIdx.x / nrg;
+  const int rg = RGW ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : blockIdx.x % nrg;
   const int n = a.lens[b];
   const int L = n - a.W;
   if (L <= 0 || (skip_kept && nothing_dropped(a, n))) return;
   const int G = a.Hq / a.Hkv;
   const int rows = G * a.W;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int slot = RGW ? (int)blockIdx.x : (int)blockIdx.x * kSnapWaves + wave;
+  const int slot = RGW ? (int)blockIdx.z : (int)blockIdx.z * kSnapWaves + wave;
   // columns whose votes are needed: the whole prefix, or (when selecting)
   // the candidates plus the pooling halo
   int vlo = 0, vhi = L;
@@ -356,7 +364,7 @@ template <int D, int NRT, bool RGW>
 static hipError_t launch_votes_t(const SnapArgs& a, const SnapWork& w, const SnapGeom& s, int skip, float* votes,
                                  hipStream_t st) {
   const float scale2 = a.scale * kLog2e;
-  const dim3 grid(s.nblk, RGW ? a.Hkv : a.Hkv * s.nrg, a.B);
+  const dim3 grid(RGW ? a.Hkv : a.Hkv * s.nrg, a.B, s.nblk);
   const dim3 block(RGW ? 64 * s.nrg : 256);
   hipLaunchKernelGGL((snap_rowstats_kernel<D, NRT, RGW>), grid, block, 0, st, a, w.row_part, s.nrg, s.slots, skip,
                      scale2);

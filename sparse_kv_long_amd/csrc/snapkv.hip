@@ -28,6 +28,10 @@
 // together, so each tile comes from HBM once and the other waves find it in
 // the CU's caches (one block per row group read every key once per group,
 // measured at eight times the algorithmic bytes for four groups).
+// Both passes are held to two waves per SIMD, which keeps the MFMA
+// accumulators in ordinary vector registers, so the next row tile's
+// matrix-core chain overlaps the current one's exponentials; in the row-
+// groups-as-waves form each wave also has its next key tile in flight.
 #include "common.h"
 #include "se_internal.h"
 
@@ -171,10 +175,8 @@ __device__ __forceinline__ void load_k_frags(const uint16_t* kbase, int kt, int 
 // a larger share of the key tiles measured no better.
 // ---------------------------------------------------------------------------
 template <int D, int NRT, bool RGW>
-__global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_rowstats_kernel(SnapArgs a,
-                                                                                    float* __restrict__ row_part,
-                                                                                    int nrg, int slots, int skip_kept,
-                                                                                    float scale2) {
+__global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+snap_rowstats_kernel(SnapArgs a, float* __restrict__ row_part, int nrg, int slots, int skip_kept, float scale2) {
   const int b = blockIdx.y;
   const int g = RGW ? blockIdx.x : blockIdx.x / nrg;
   const int rg = RGW ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : blockIdx.x % nrg;
@@ -204,9 +206,7 @@ __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_rowstats_ke
   }
   const uint16_t* kbase = a.k + ((int64_t)b * a.Hkv + g) * a.N * D;
   const int tiles = (n + 31) / 32;
-  for (int kt = slot; kt < tiles; kt += slots) {
-    uint4 kf[D / 16];
-    load_k_frags<D>(kbase, kt, n, kf);
+  auto tile = [&](const uint4(&kf)[D / 16], int kt) {
     const bool edge = kt * 32 + 31 >= L;  // tile reaches the window (or the end): mask per element
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
@@ -245,6 +245,26 @@ __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_rowstats_ke
         l[rt] = l[rt] * __builtin_amdgcn_exp2f(m[rt] - mn) + s;
         m[rt] = mn;
       }
+    }
+  };
+  if constexpr (RGW) {
+    // two key-fragment sets in turn: the walker's next tile is in flight
+    // while this one is reduced (past the end the last tile is fetched
+    // again, a cache hit, and not used)
+    uint4 ka[D / 16], kb[D / 16];
+    if (slot < tiles) load_k_frags<D>(kbase, slot, n, ka);
+    for (int kt = slot; kt < tiles; kt += 2 * slots) {
+      load_k_frags<D>(kbase, min(kt + slots, tiles - 1), n, kb);
+      tile(ka, kt);
+      if (kt + slots >= tiles) break;
+      load_k_frags<D>(kbase, min(kt + 2 * slots, tiles - 1), n, ka);
+      tile(kb, kt + slots);
+    }
+  } else {
+    for (int kt = slot; kt < tiles; kt += slots) {
+      uint4 kf[D / 16];
+      load_k_frags<D>(kbase, kt, n, kf);
+      tile(kf, kt);
     }
   }
   // combine the two lane halves (same rows, other 16 keys of each tile)
@@ -294,11 +314,9 @@ __device__ __forceinline__ float row_normaliser(const float* __restrict__ row_pa
 // votes layout [nrg, B, Hkv, N].
 // ---------------------------------------------------------------------------
 template <int D, int NRT, bool RGW>
-__global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_votes_kernel(SnapArgs a,
-                                                                                 const float* __restrict__ row_part,
-                                                                                 float* __restrict__ votes, int nrg,
-                                                                                 int slots, int skip_kept,
-                                                                                 float scale2) {
+__global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+snap_votes_kernel(SnapArgs a, const float* __restrict__ row_part, float* __restrict__ votes, int nrg, int slots,
+                  int skip_kept, float scale2) {
   __shared__ float c_lds[RGW ? kMaxRgWaves : 1][kRowsPerGroup];
   const int b = blockIdx.y;
   const int g = RGW ? blockIdx.x : blockIdx.x / nrg;
@@ -336,9 +354,13 @@ __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_votes_kerne
   // the slot's tiles in descending order: pass 1 read them ascending, so the
   // ones it read last (the likeliest still in the caches) come first
   const int kt_last = slot < tiles ? t0 + slot + (tiles - 1 - slot) / slots * slots : -1;
-  for (int kt = kt_last; kt >= t0; kt -= slots) {
-    uint4 kf[D / 16];
-    load_k_frags<D>(kbase, kt, n, kf);
+  auto tile = [&](const uint4(&kf)[D / 16], int kt) {
+    // with the next tile in flight (below), the normalisers are read from
+    // LDS at each tile rather than held in registers, which leaves room for
+    // the second set of key fragments
+    int lds_off = 0;
+    if constexpr (RGW) asm volatile("" : "+v"(lds_off));
+    const float* cwt = cw + lds_off;
     float vote = 0.f;
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
@@ -347,7 +369,7 @@ __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_votes_kerne
       for (int ks = 0; ks < D / 16; ++ks) acc = mfma32(qf[rt][ks], kf[ks], acc);
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 c4 = *reinterpret_cast<const float4*>(&cw[rt * 32 + 8 * r4 + 4 * (lane >> 5)]);
+        const float4 c4 = *reinterpret_cast<const float4*>(&cwt[rt * 32 + 8 * r4 + 4 * (lane >> 5)]);
         vote += __builtin_amdgcn_exp2f(acc[4 * r4 + 0] * scale2 - c4.x);
         vote += __builtin_amdgcn_exp2f(acc[4 * r4 + 1] * scale2 - c4.y);
         vote += __builtin_amdgcn_exp2f(acc[4 * r4 + 2] * scale2 - c4.z);
@@ -357,6 +379,24 @@ __global__ __launch_bounds__(RGW ? 64 * kMaxRgWaves : 256) void snap_votes_kerne
     vote += __shfl_xor(vote, 32);
     const int key = kt * 32 + lane;
     if (lane < 32 && key < L) vrow[key] = vote;
+  };
+  if constexpr (RGW) {
+    // two key-fragment sets in turn, as in pass 1
+    uint4 ka[D / 16], kb[D / 16];
+    if (kt_last >= t0) load_k_frags<D>(kbase, kt_last, n, ka);
+    for (int kt = kt_last; kt >= t0; kt -= 2 * slots) {
+      load_k_frags<D>(kbase, max(kt - slots, t0), n, kb);
+      tile(ka, kt);
+      if (kt - slots < t0) break;
+      load_k_frags<D>(kbase, max(kt - 2 * slots, t0), n, ka);
+      tile(kb, kt - slots);
+    }
+  } else {
+    for (int kt = kt_last; kt >= t0; kt -= slots) {
+      uint4 kf[D / 16];
+      load_k_frags<D>(kbase, kt, n, kf);
+      tile(kf, kt);
+    }
   }
 }
 

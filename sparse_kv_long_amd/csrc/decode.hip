@@ -339,9 +339,12 @@ struct MfmaDecodeShape {
 //         -- the weights stay in the lanes that computed them, and the value
 //         rows are loaded whole (16 lanes per 256-byte row) and repacked
 //         in-lane with v_perm_b32.
+// Two waves per SIMD, declared as such: the accumulators then live in
+// ordinary vector registers, with no copies into and out of the
+// accumulation registers (measured 0.3-0.8 us faster at 128K and 32K).
 template <int G, int NW, bool FINAL>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs,
-                                                              int64_t ts, int pps, float scale2) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void
+decode_mfma_kernel(DecodeArgs a, int Hkv, int64_t ps, int64_t hs, int64_t ts, int pps, float scale2) {
   constexpr int D = 128, PPS = MfmaDecodeShape<G>::PPS;
   static_assert(G <= 16, "one 16-row head tile");
   __shared__ float head_ml[16][2];  // FINAL: per head, the max and the weight sum over the waves

@@ -24,6 +24,11 @@ CASES = {
                     [1500, 900, 401], 0, 200, None),
     "h2o_w128_g8_d64": (SnapKVWorkload("e_h2o64", 2, 8, 1, 64, 1200, 128, 1, 150, 0, seed=43),
                         [1200, 640], 0, 150, None),
+    # enough (request, KV head) units that each key-tile walker of the
+    # row-groups-as-waves passes takes several tiles (one to six, odd and even
+    # counts), so the loop that keeps the next tile in flight runs every branch
+    "h2o_w128_multitile": (SnapKVWorkload("e_h2o_mt", 4, 32, 8, 128, 3000, 128, 1, 300, 0, seed=49),
+                           [3000, 2500, 1000, 520], 0, 300, None),
     # edge lengths: empty, shorter than the window, exactly the window, exactly
     # sink + recent (nothing to choose from), one candidate past the budget
     "edges_sink_recent": (SnapKVWorkload("e_edge", 7, 8, 2, 128, 400, 16, 5, 30, 0, seed=47),
@@ -100,11 +105,13 @@ def test_eviction_family_matches_oracle(name):
             assert not ko[b, g, kl:].any()
 
 
-def test_h2o_votes_match_oracle():
+@pytest.mark.parametrize("name", ["h2o_w128_g4", "h2o_w128_multitile"])
+def test_h2o_votes_match_oracle(name):
     """The 128-row window's votes themselves (four row groups of 128 rows)."""
-    wl, lens, _, _, _ = CASES["h2o_w128_g4"]
+    wl, lens, sink, recent, iv = CASES[name]
+    announce(f"h2o votes case {name} seed {wl.seed} lens {lens}")
     x = make_snapkv_inputs(wl, DEV, prompt_lens=lens, with_decode=False)
-    p, _ = params(wl, 0, 200, None)
+    p, _ = params(wl, sink, recent, iv)
     ws = workspace(se.se_snapkv_workspace_size(p))
     votes = torch.full((wl.batch, wl.num_kv_heads, wl.prompt), float("nan"), device=DEV)
     call_twice(lambda: se.se_snapkv_votes(p, x["q_win"], x["k"], x["prompt_lens"], votes, ws), ws, [votes], "h2o votes")
